@@ -1,0 +1,176 @@
+/*
+ * moe.h - C ABI of an MI355X (gfx950) library for one GPU's share of an expert-parallel
+ * Mixture-of-Experts layer:  route -> permute -> grouped SwiGLU FFN -> combine.
+ *
+ * The operation is the one the "Expert Parallelism" tutorial page describes in section 1
+ * (What is it?: E expert FFNs per layer, each token routed to k of them) and section 4
+ * (The All-to-All: the router names each token's experts; tokens are sorted by destination
+ * expert and counted so that every expert holds a contiguous block of rows; a grouped GEMM
+ * runs every expert over its rows; results return to the original token order and the k
+ * expert outputs of a token are summed with their gate weights). On one GPU the exchange
+ * steps are the identity, so dispatch is the expert sort and combine is its inverse.
+ *
+ * Conventions shared by every call
+ *  - Memory: every pointer argument is a device pointer allocated by the caller (the
+ *    library never allocates or frees device memory and keeps no per-call state). Buffers
+ *    must not overlap unless stated.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call
+ *    only enqueues work on that stream and returns; it never synchronises. Results are
+ *    valid once the stream has reached that point.
+ *  - Errors: all arguments are checked on the host before anything is enqueued; on any
+ *    error nothing is enqueued and a status other than MOE_OK is returned. A failed kernel
+ *    launch returns MOE_ERR_HIP. Device-side faults surface at the caller's next
+ *    synchronisation. Device-resident index data produced by one call and consumed by
+ *    another (ids, offsets, maps) must be what the producing call wrote; kernels clamp such
+ *    indices so that corrupt values never address memory out of bounds, but the results
+ *    are then unspecified.
+ *  - Sizes: T tokens, E experts, k experts per token, d hidden size, d_ff expert width,
+ *    R = T*k routed rows. Limits: 0 <= T, 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E,
+ *    MOE_MAX_TOPK), T*k*max(d, d_ff) < 2^31. T = 0 is a valid empty call.
+ *  - Alignment: every pointer 16-byte aligned.
+ *  - Determinism: no floating-point atomics; repeated calls give bit-identical results.
+ *
+ * Number formats (moe_dtype_t): fp32, bf16, and OCP fp8 e4m3fn (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, max 448) for weights only.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, size out of range, bad combination */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than the *_workspace_size */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3FN = 2 } moe_dtype_t;
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/* Text for a status code (static storage; never NULL). */
+const char* moe_status_string(moe_status_t status);
+
+/*
+ * moe_route - router output to top-k experts and gate weights (tutorial page, section 4:
+ * the router's per-token choice of experts; section 1: each token goes to k of E experts;
+ * section 4, combine: the weights of the weighted sum).
+ *
+ *   logits     [T, E] fp32, row-major, finite (non-finite values give unspecified ids).
+ *   topk_ids   [T, k] int32 out: for each token the k largest logits in descending order;
+ *              equal logits go to the lower expert index (+0.0 equals -0.0).
+ *   topk_gates [T, k] fp32 out: softmax over the k chosen logits,
+ *              g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) (equal to the full softmax
+ *              renormalised over the top k); sums to 1 within k * 2^-23.
+ *   counts     [E] int32 out, or NULL: number of rows routed to each expert (the histogram
+ *              of topk_ids; overwritten, not accumulated).
+ */
+moe_status_t moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                       float* topk_gates, int32_t* counts, void* stream);
+
+/* Bytes of workspace moe_permute needs (0 is possible; then workspace may be NULL). */
+size_t moe_permute_workspace_size(int T, int E, int k);
+
+/*
+ * moe_permute - sort the T*k assignments by destination expert, count them and copy every
+ * token's row into expert-contiguous order (tutorial page, section 4, dispatch: sort by
+ * destination expert, count per destination, contiguous rows per expert; section 9: unsorted
+ * rows mean uncoalesced access).
+ *
+ *   x              [T, d] in x_dtype (MOE_F32 or MOE_BF16), row-major.
+ *   topk_ids       [T, k] int32, each in [0, E) (as written by moe_route).
+ *   counts         [E] int32 out: rows per expert.
+ *   offsets        [E+1] int32 out: exclusive scan of counts; offsets[E] = T*k.
+ *   sorted_to_flat [T*k] int32 out: sorted row r holds flat assignment i = t*k + j.
+ *   flat_to_sorted [T*k] int32 out: inverse permutation of sorted_to_flat.
+ *   x_sorted       [T*k, d] in x_dtype out: x_sorted[r] = x[sorted_to_flat[r] / k] (a bit
+ *                  copy). Within one expert, rows are in increasing flat index (stable sort).
+ *   workspace      >= moe_permute_workspace_size(T, E, k) bytes, 16-byte aligned.
+ *   Requires d*sizeof(x_dtype) to be a multiple of 16.
+ */
+moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, const int32_t* topk_ids, int T,
+                         int E, int k, int d, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace moe_grouped_ffn needs (holds the SwiGLU activations h [rows, d_ff] in
+ * act_dtype between the two GEMMs, plus a small schedule). */
+size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_dtype,
+                              moe_dtype_t w_dtype);
+
+/*
+ * moe_grouped_ffn - every expert's SwiGLU FFN over its contiguous rows, all experts in one
+ * grouped launch per GEMM (tutorial page, section 4, compute: a grouped GEMM, many
+ * differently shaped GEMMs in one launch; section 8: grouped-GEMM quality matters; the
+ * makespan-dispatcher abstract on the UltraEP-titled page: below roughly 156-168 rows an
+ * expert's time is weight streaming, above it GEMM tiles).
+ *
+ * For expert e and rows r in [offsets[e], offsets[e+1]):
+ *     h[r]        = silu(x_sorted[r] . Wg_e) * (x_sorted[r] . Wu_e),  silu(z) = z/(1+e^-z)
+ *     y_sorted[r] = h[r] . Wd_e
+ *
+ *   x_sorted  [rows, d] in act_dtype (MOE_F32 or MOE_BF16).
+ *   offsets   [E+1] int32, non-decreasing, offsets[0] = 0, offsets[E] = rows.
+ *   w_gate, w_up [E, d_ff, d] in w_dtype; w_down [E, d, d_ff] in w_dtype. Each matrix is
+ *             stored with its contraction axis contiguous (the transpose of the math-side
+ *             Wg, Wu [d, d_ff] and Wd [d_ff, d]).
+ *   w_dtype   MOE_F32 with act MOE_F32; MOE_BF16 or MOE_FP8_E4M3FN with act MOE_BF16.
+ *   s_gate, s_up [E, ceil(d_ff/128), ceil(d/128)], s_down [E, ceil(d/128), ceil(d_ff/128)]
+ *             fp32 per-128x128-block scales of the stored matrices (fp8 only, else NULL):
+ *             the weight value is code * scale of its block.
+ *   y_sorted  [rows, d] fp32 out.
+ *   Arithmetic: fp32 accumulation; with act MOE_BF16, h is rounded to bf16 (RNE) between
+ *   the two GEMMs; fp8 codes are converted exactly and the block scale multiplies the fp32
+ *   partial sum of each 128-long contraction block.
+ *   Requires d and d_ff multiples of 8 (of 128 for fp8). Experts with no rows are never read.
+ */
+moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const int32_t* offsets,
+                             int rows, int E, int d, int d_ff, const void* w_gate,
+                             const void* w_up, const void* w_down, moe_dtype_t w_dtype,
+                             const float* s_gate, const float* s_up, const float* s_down,
+                             float* y_sorted, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * moe_combine - return the expert outputs to token order and take each token's gate-weighted
+ * sum (tutorial page, section 4, combine).
+ *
+ *   y[t] = sum_{j=0..k-1} topk_gates[t, j] * y_sorted[flat_to_sorted[t*k + j]]
+ *   summed in fp32 in slot order j = 0..k-1.
+ *
+ *   y_sorted [T*k, d] fp32; flat_to_sorted [T*k] int32; topk_gates [T, k] fp32;
+ *   y [T, d] fp32 out. Requires d a multiple of 4.
+ */
+moe_status_t moe_combine(const float* y_sorted, const int32_t* flat_to_sorted,
+                         const float* topk_gates, int T, int k, int d, float* y, void* stream);
+
+/* Bytes of workspace moe_layer needs. */
+size_t moe_layer_workspace_size(int T, int E, int k, int d, int d_ff, moe_dtype_t act_dtype,
+                                moe_dtype_t w_dtype);
+
+/*
+ * moe_layer - the whole layer on one stream: moe_route, moe_permute, moe_grouped_ffn and
+ * moe_combine in order, with every intermediate written to a caller buffer so that each can
+ * be checked. Arguments have the meanings given above; x and x_sorted are in act_dtype.
+ */
+moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype, int T, int E,
+                       int k, int d, int d_ff, const void* w_gate, const void* w_up,
+                       const void* w_down, moe_dtype_t w_dtype, const float* s_gate,
+                       const float* s_up, const float* s_down, int32_t* topk_ids,
+                       float* topk_gates, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                       float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,402 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code.
+
+Each check ties the oracle to something other than itself: values the pages print for a
+worked example (tests/golden/), library routines that compute the same definition (stable
+argsort, bincount, cumsum, softmax, torch's format conversions), closed forms, invariants
+and a dense all-experts brute force on tiny inputs. The mutation test at the end plants
+plausible mistakes in the oracle (on the CPU) and checks that these pins catch every one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import moe_oracle as om
+import synth
+from token_dispatch_expert_amd import traffic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------------------
+# tiny workloads
+# ----------------------------------------------------------------------------------------
+def tiny_case(T, d, E, k, d_ff, seed, fmt="f32", ties=False):
+    rng = np.random.default_rng(seed)
+    if ties:
+        logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    else:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    W = {e: dict(gate=(rng.standard_normal((d_ff, d)) / math.sqrt(d)).astype(np.float32),
+                 up=(rng.standard_normal((d_ff, d)) / math.sqrt(d)).astype(np.float32),
+                 down=(rng.standard_normal((d, d_ff)) / math.sqrt(d_ff)).astype(np.float32))
+         for e in range(E)}
+    return logits, x, W
+
+
+def brute_force_layer(logits, x, W, k):
+    """Dense all-experts-masked evaluation written independently of the oracle: every expert
+    runs on every token (einsum over the stored layouts), a 0/1 mask from a stable argsort
+    picks the top k, and the gates come from a full softmax renormalised over the top k."""
+    l = logits.astype(np.float64)
+    T, E = l.shape
+    order = np.argsort(-l, axis=1, kind="stable")[:, :k]
+    p = scipy.special.softmax(l, axis=1)
+    M = np.zeros((T, E))
+    for t in range(T):
+        sel = p[t, order[t]]
+        M[t, order[t]] = sel / sel.sum()
+    X = x.astype(np.float64)
+    y = np.zeros_like(X)
+    for e in range(E):
+        g = np.einsum("td,fd->tf", X, W[e]["gate"].astype(np.float64))
+        u = np.einsum("td,fd->tf", X, W[e]["up"].astype(np.float64))
+        hh = g * scipy.special.expit(g) * u
+        ye = np.einsum("tf,df->td", hh, W[e]["down"].astype(np.float64))
+        y += M[:, e:e + 1] * ye
+    return y, order, M
+
+
+def run_oracle(logits, x, W, k):
+    return oracle.layer(logits, x, "f32", lambda e: W[e], "f32", k)
+
+
+# ----------------------------------------------------------------------------------------
+# checks (each returns normally or raises); collected so the mutation test can re-run them
+# ----------------------------------------------------------------------------------------
+def check_decode_bf16():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.decode_bf16(bits)
+    ok = np.isnan(ref) == np.isnan(got)
+    assert ok.all()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def check_decode_e4m3fn():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_e4m3fn(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def check_route_vs_stable_argsort():
+    for seed, ties in [(0, False), (1, True), (2, True), (3, False)]:
+        for (T, E, k) in [(9, 8, 1), (9, 8, 3), (5, 16, 16), (17, 33, 5)]:
+            logits, _, _ = tiny_case(T, 4, E, k, 4, seed, ties=ties)
+            ids, _ = oracle.route(logits, k)
+            ref = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k]
+            assert np.array_equal(ids, ref)
+
+
+def check_route_special_cases():
+    # all-equal logits -> 0..k-1, equal gates
+    ids, g = oracle.route(np.full((3, 6), 0.25, np.float32), 4)
+    assert np.array_equal(ids, np.tile(np.arange(4), (3, 1)))
+    assert np.allclose(g, 0.25, rtol=0, atol=1e-15)
+    # +0.0 and -0.0 are equal: the lower index wins either way round
+    lg = np.array([[-0.0, 0.0, -1.0], [0.0, -0.0, -1.0]], np.float32)
+    ids, _ = oracle.route(lg, 2)
+    assert np.array_equal(ids, [[0, 1], [0, 1]])
+    # k = 1: gate is exactly 1
+    logits, _, _ = tiny_case(11, 4, 7, 1, 4, 5)
+    _, g = oracle.route(logits, 1)
+    assert np.all(g == 1.0)
+    # k = E: the gates are the full softmax, in descending order
+    ids, g = oracle.route(logits, 7)
+    full = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    assert np.allclose(g, np.take_along_axis(full, ids.astype(np.int64), axis=1), rtol=1e-13, atol=0)
+    # gates sum to one and are non-increasing; ids are distinct
+    ids, g = oracle.route(logits, 3)
+    assert np.allclose(g.sum(1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(g, axis=1) <= 0)
+    assert all(len(set(r)) == 3 for r in ids.tolist())
+    # a constant added to a row changes neither ids nor gates (shift invariance)
+    ids2, g2 = oracle.route(logits + np.float32(4.0), 3)
+    assert np.array_equal(ids, ids2)
+    assert np.allclose(g, g2, rtol=1e-6, atol=0)
+    # a two-expert closed form: gates = sigmoid of the logit gap
+    ids, g = oracle.route(np.array([[0.5, 2.0]], np.float32), 2)
+    assert np.array_equal(ids, [[1, 0]])
+    assert math.isclose(g[0, 1], 1.0 / (1.0 + math.exp(1.5)), rel_tol=1e-14)
+
+
+def check_permute_vs_library():
+    for seed, (T, E, k) in enumerate([(13, 8, 2), (40, 5, 5), (1, 4, 3), (64, 16, 1)]):
+        logits, _, _ = tiny_case(T, 4, E, k, 4, seed, ties=True)
+        ids, _ = oracle.route(logits, k)
+        p = oracle.permute(ids, E)
+        flat = ids.reshape(-1)
+        assert np.array_equal(p["counts"], np.bincount(flat, minlength=E))
+        assert np.array_equal(p["offsets"], np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        assert np.array_equal(p["sorted_to_flat"], np.argsort(flat, kind="stable"))
+        # bijection, inverse, contiguity, totals
+        assert np.array_equal(np.sort(p["sorted_to_flat"]), np.arange(T * k))
+        assert np.array_equal(p["flat_to_sorted"][p["sorted_to_flat"]], np.arange(T * k))
+        assert p["counts"].sum() == T * k
+        for e in range(E):
+            a, b = p["offsets"][e], p["offsets"][e + 1]
+            assert np.all(flat[p["sorted_to_flat"][a:b]] == e)
+
+
+def check_golden_load_example():
+    g = _golden("load_imbalance_example.json")
+    E, T = g["experts"], g["tokens"]
+    counts = np.array(g["counts"])
+    assert counts.sum() == T
+    # logits that make expert e the arg-max for exactly counts[e] tokens, in a scrambled order
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(7).shuffle(owner)
+    logits = np.random.default_rng(8).uniform(-1, 0, size=(T, E)).astype(np.float32)
+    logits[np.arange(T), owner] = 1.0
+    ids, gates = oracle.route(logits, 1)
+    p = oracle.permute(ids, E)
+    assert np.array_equal(p["counts"], counts)
+    assert p["offsets"].tolist() == [0, 140, 235, 313, 375, 423, 463, 494, 512]
+    ideal = T // E
+    assert ideal == g["balanced_per_expert"]
+    assert f"{p['counts'].max() / ideal:.1f}x" == g["hot_vs_balanced_printed"]
+    assert round(100 * ideal / p["counts"].max()) == g["utilisation_printed_percent"]
+    assert np.all(gates == 1.0)
+
+
+def check_golden_volume_example():
+    g = _golden("a2a_volume_example.json")
+    per_layer = traffic.exchange_bytes_per_layer(g["tokens"], g["k"], g["d"], g["bytes_per_element"])
+    assert per_layer == 2_097_152
+    assert round(per_layer / 1e6, 1) == g["per_layer_printed_MB"]
+    per_step = per_layer * g["layers"]
+    assert round(per_step / 1e6) == g["per_step_printed_MB"]
+    for link in g["links"]:
+        ms = traffic.transfer_ms(per_step, link["GB_per_s"])
+        digits = len(str(link["printed_ms"]).split(".")[1])
+        assert round(ms, digits) == link["printed_ms"], (link, ms)
+
+
+def check_swiglu_closed_form():
+    # one expert, one token, d = d_ff = 1: y = c * silu(a x) * (b x)
+    x = np.array([[2.0]], np.float32)
+    W = {0: dict(gate=np.array([[0.5]], np.float32), up=np.array([[3.0]], np.float32),
+                 down=np.array([[-1.0]], np.float32))}
+    out = run_oracle(np.zeros((1, 1), np.float32), x, W, 1)
+    expect = -1.0 * (1.0 / (1.0 + math.exp(-1.0))) * 6.0
+    assert math.isclose(out["y"][0, 0], expect, rel_tol=1e-15)
+    # gate and up are not interchangeable: silu sits on the gate branch only
+    W2 = {0: dict(gate=np.array([[1.0, 0.0]], np.float32), up=np.array([[0.0, 1.0]], np.float32),
+                  down=np.array([[1.0], [0.0]], np.float32))}
+    out = run_oracle(np.zeros((1, 1), np.float32), np.array([[-1.0, 2.0]], np.float32), W2, 1)
+    sil = -1.0 / (1.0 + math.exp(1.0))
+    assert np.allclose(out["y"][0], [sil * 2.0, 0.0], rtol=1e-15, atol=0)
+
+
+def check_brute_force_layer():
+    shapes = [(7, 6, 5, 9), (16, 16, 8, 16), (3, 5, 4, 12), (10, 8, 8, 8)]
+    for seed, (T, d, E, d_ff) in enumerate(shapes):
+        for k in range(1, E + 1):
+            logits, x, W = tiny_case(T, d, E, k, d_ff, 100 + seed, ties=(seed % 2 == 1))
+            ref, order, _ = brute_force_layer(logits, x, W, k)
+            out = run_oracle(logits, x, W, k)
+            assert np.array_equal(out["topk_ids"], order)
+            assert oracle.rel_max_err(out["y"], ref) < 1e-12, (T, d, E, d_ff, k)
+
+
+def check_identity_experts_and_gather():
+    logits, x, _ = tiny_case(12, 10, 6, 3, 4, 9)
+    ids, gates = oracle.route(logits, 3)
+    p = oracle.permute(ids, 6)
+    xs = oracle.gather_rows(x, p["sorted_to_flat"], 3)
+    # identity experts + normalised gates return the input
+    y = oracle.combine(xs.astype(np.float64), p["flat_to_sorted"], gates)
+    assert np.allclose(y, x.astype(np.float64), rtol=1e-14, atol=1e-14)
+    # k = 1 puts every row back exactly
+    ids1, g1 = oracle.route(logits, 1)
+    p1 = oracle.permute(ids1, 6)
+    xs1 = oracle.gather_rows(x, p1["sorted_to_flat"], 1)
+    y1 = oracle.combine(xs1.astype(np.float64), p1["flat_to_sorted"], g1)
+    assert np.array_equal(y1, x.astype(np.float64))
+    # rows of x_sorted are copies of their token's row
+    for r in range(len(xs)):
+        assert np.array_equal(xs[r], x[p["sorted_to_flat"][r] // 3])
+
+
+def check_fp8_dequant_blocks():
+    # a 256x256 matrix in 2x2 blocks with distinct scales: value = code value * its block scale
+    codes = np.full((256, 256), 0x38, np.uint8)  # 1.0
+    codes[0, 0] = 0xB8  # -1.0
+    scale = np.array([[2.0, 3.0], [5.0, 7.0]], np.float32)
+    v = oracle.decode_matrix(codes, "fp8_e4m3fn", scale)
+    assert v[0, 0] == -2.0 and v[1, 1] == 2.0 and v[0, 200] == 3.0 and v[200, 0] == 5.0 and v[255, 255] == 7.0
+
+
+def check_bf16_layer_decodes_inputs():
+    # the bf16 path decodes stored bit patterns exactly before any arithmetic
+    cfg = synth.tiny_config(T=5, d=16, E=4, k=2, d_ff=32, act="bf16", w="bf16", seed=3)
+    logits, xb = synth.make_routing_inputs(cfg)
+    Wb = {e: synth.make_expert_weights(cfg, e) for e in range(cfg.E)}
+    out = oracle.layer(logits, xb, "bf16", lambda e: Wb[e], "bf16", cfg.k)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    Wf = {e: {n: torch.from_numpy(Wb[e][n].view(np.int16)).view(torch.bfloat16).float().numpy()
+              for n in ("gate", "up", "down")} for e in range(cfg.E)}
+    ref, _, _ = brute_force_layer(logits, xf, Wf, cfg.k)
+    assert oracle.rel_max_err(out["y"], ref) < 1e-12
+
+
+CHECKS = [
+    check_decode_bf16, check_decode_e4m3fn, check_route_vs_stable_argsort,
+    check_route_special_cases, check_permute_vs_library, check_golden_load_example,
+    check_golden_volume_example, check_swiglu_closed_form, check_brute_force_layer,
+    check_identity_experts_and_gather, check_fp8_dequant_blocks, check_bf16_layer_decodes_inputs,
+]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
+def test_oracle_pin(check):
+    check()
+
+
+# ----------------------------------------------------------------------------------------
+# the pins must catch plausible mistakes planted in the oracle
+# ----------------------------------------------------------------------------------------
+_ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16")}
+
+
+def _mut_route_tie_high(logits, k):
+    lg = np.asarray(logits, np.float32).astype(np.float64)
+    T, E = lg.shape
+    ids = np.empty((T, k), np.int32)
+    gates = np.empty((T, k))
+    for t in range(T):
+        row = lg[t].copy()
+        ch = []
+        for _ in range(k):
+            e = E - 1 - int(np.argmax(row[::-1]))   # last occurrence wins ties
+            ch.append(e)
+            row[e] = -np.inf
+        w = np.exp(lg[t, ch] - lg[t, ch[0]])
+        ids[t], gates[t] = ch, w / w.sum()
+    return ids, gates
+
+
+def _mut_route_full_softmax(logits, k):
+    ids, _ = _ORIG["route"](logits, k)
+    lg = np.asarray(logits, np.float32).astype(np.float64)
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    return ids, np.take_along_axis(p, ids.astype(np.int64), 1)
+
+
+def _mut_route_smallest(logits, k):
+    ids, g = _ORIG["route"](-np.asarray(logits, np.float32), k)
+    return ids, g
+
+
+def _mut_route_no_max_shift_sign(logits, k):
+    ids, _ = _ORIG["route"](logits, k)
+    lg = np.asarray(logits, np.float32).astype(np.float64)
+    sel = np.take_along_axis(lg, ids.astype(np.int64), 1)
+    w = np.exp(sel[:, :1] - sel)       # wrong sign
+    return ids, w / w.sum(1, keepdims=True)
+
+
+def _mut_permute_unstable(topk_ids, E):
+    p = _ORIG["permute"](topk_ids, E)
+    s2f = p["sorted_to_flat"].copy()
+    for e in range(E):
+        a, b = p["offsets"][e], p["offsets"][e + 1]
+        s2f[a:b] = s2f[a:b][::-1]
+    f2s = np.empty_like(s2f)
+    f2s[s2f] = np.arange(len(s2f))
+    return dict(p, sorted_to_flat=s2f, flat_to_sorted=f2s.astype(np.int32))
+
+
+def _mut_permute_inclusive_scan(topk_ids, E):
+    p = _ORIG["permute"](topk_ids, E)
+    off = p["offsets"].copy()
+    off[:-1] = off[1:]
+    return dict(p, offsets=off)
+
+
+def _mut_ffn_silu_on_up(X, Wg, Wu, Wd, return_h=False):
+    G, U = X @ Wg.T, X @ Wu.T
+    h = om.silu(U) * G
+    y = h @ Wd.T
+    return (y, h) if return_h else y
+
+
+def _mut_ffn_sigmoid_only(X, Wg, Wu, Wd, return_h=False):
+    G, U = X @ Wg.T, X @ Wu.T
+    h = (1.0 / (1.0 + np.exp(-G))) * U
+    y = h @ Wd.T
+    return (y, h) if return_h else y
+
+
+def _mut_ffn_down_untransposed(X, Wg, Wu, Wd, return_h=False):
+    G, U = X @ Wg.T, X @ Wu.T
+    h = om.silu(G) * U
+    y = h @ Wd if Wd.shape[0] == Wd.shape[1] else h @ Wd.T[:, ::-1]
+    return (y, h) if return_h else y
+
+
+def _mut_combine_unweighted(y_sorted, flat_to_sorted, gates):
+    return _ORIG["combine"](y_sorted, flat_to_sorted, np.ones_like(gates))
+
+
+def _mut_combine_wrong_map(y_sorted, flat_to_sorted, gates):
+    inv = np.empty_like(flat_to_sorted)
+    inv[flat_to_sorted] = np.arange(len(flat_to_sorted))
+    return _ORIG["combine"](y_sorted, inv, gates)
+
+
+def _mut_decode_bf16_shift(bits):
+    u32 = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(15)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _mut_decode_e4m3_bias8(codes):
+    return _ORIG["decode_e4m3fn"](codes) / 2.0
+
+
+MUTANTS = {
+    "route_tie_high": ("route", _mut_route_tie_high),
+    "route_full_softmax": ("route", _mut_route_full_softmax),
+    "route_smallest": ("route", _mut_route_smallest),
+    "route_gate_sign": ("route", _mut_route_no_max_shift_sign),
+    "permute_unstable": ("permute", _mut_permute_unstable),
+    "permute_inclusive_scan": ("permute", _mut_permute_inclusive_scan),
+    "ffn_silu_on_up": ("expert_ffn", _mut_ffn_silu_on_up),
+    "ffn_sigmoid_only": ("expert_ffn", _mut_ffn_sigmoid_only),
+    "ffn_down_untransposed": ("expert_ffn", _mut_ffn_down_untransposed),
+    "combine_unweighted": ("combine", _mut_combine_unweighted),
+    "combine_wrong_map": ("combine", _mut_combine_wrong_map),
+    "decode_bf16_shift": ("decode_bf16", _mut_decode_bf16_shift),
+    "decode_e4m3_bias8": ("decode_e4m3fn", _mut_decode_e4m3_bias8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    fn_name, mutant = MUTANTS[name]
+    monkeypatch.setattr(om, fn_name, mutant)
+    monkeypatch.setattr(oracle, fn_name, mutant, raising=False)
+    failures = 0
+    for check in CHECKS:
+        try:
+            check()
+        except Exception:  # an assertion or a shape error both count as caught
+            failures += 1
+    assert failures > 0, f"no pin caught mutant {name}"

@@ -1,0 +1,85 @@
+"""Algorithmic byte and flop counts of the MoE layer's steps (host-side arithmetic only).
+
+These are the bytes each step *must* move and the flops it must do, independent of how a
+kernel is written; achieved bandwidth / MFMA rate are these divided by measured time.
+
+The dispatch volume follows the "Expert Parallelism" tutorial page, section 4 (The
+All-to-All, communication volume): every token sends k rows of d elements one way and gets
+k rows back, so one direction moves tokens * k * d * bytes.
+"""
+from __future__ import annotations
+
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}
+
+
+def dispatch_bytes(tokens: int, k: int, d: int, elem_bytes: int) -> int:
+    """One direction of the dispatch (or combine) exchange: tokens * k * d * bytes."""
+    return tokens * k * d * elem_bytes
+
+
+def exchange_bytes_per_layer(tokens: int, k: int, d: int, elem_bytes: int) -> int:
+    """Dispatch plus combine for one MoE layer."""
+    return 2 * dispatch_bytes(tokens, k, d, elem_bytes)
+
+
+def transfer_ms(nbytes: float, gb_per_s: float) -> float:
+    return nbytes / (gb_per_s * 1e9) * 1e3
+
+
+def route_bytes(T: int, E: int, k: int) -> int:
+    """logits f32 [T,E] read; ids i32 and gates f32 [T,k] written."""
+    return T * E * 4 + T * k * 8
+
+
+def permute_bytes(T: int, E: int, k: int, d: int, a: int) -> int:
+    """x read once per token, x_sorted written once per assignment, ids read, both index maps
+    written, counts and offsets written."""
+    R = T * k
+    return T * d * a + R * d * a + R * 4 + 2 * R * 4 + (2 * E + 1) * 4
+
+
+def scatter_copy_bytes(T: int, k: int, d: int, a: int) -> int:
+    """The row-copy part of the permutation: x read once, x_sorted written k times."""
+    return T * d * a + T * k * d * a
+
+
+def gate_up_bytes(active: int, R: int, d: int, d_ff: int, w: float, a: int, h: int,
+                  scale_bytes: int = 0) -> int:
+    """Gate/up pass: gate and up weights of every expert with rows, x_sorted read, h written."""
+    return int(active * 2 * d * d_ff * w) + active * 2 * scale_bytes + R * d * a + R * d_ff * h
+
+
+def down_bytes(active: int, R: int, d: int, d_ff: int, w: float, h: int,
+               scale_bytes: int = 0) -> int:
+    """Down pass: down weights of every expert with rows, h read, y_sorted (fp32) written."""
+    return int(active * d * d_ff * w) + active * scale_bytes + R * d_ff * h + R * d * 4
+
+
+def ffn_bytes(active: int, R: int, d: int, d_ff: int, w: float, a: int,
+              scale_bytes_per_matrix: int = 0) -> int:
+    """Layer-level FFN bytes: weights of active experts, x_sorted read, y_sorted (fp32) written
+    (the h round trip between the two GEMMs is not counted: it is an implementation choice)."""
+    return int(active * 3 * d * d_ff * w) + active * 3 * scale_bytes_per_matrix + R * d * a + R * d * 4
+
+
+def fp8_scale_bytes(d: int, d_ff: int) -> int:
+    return -(-d // 128) * -(-d_ff // 128) * 4
+
+
+def ffn_flops(R: int, d: int, d_ff: int) -> int:
+    """Three GEMMs of R x d x d_ff: gate, up and down."""
+    return 6 * R * d * d_ff
+
+
+def gate_up_flops(R: int, d: int, d_ff: int) -> int:
+    return 4 * R * d * d_ff
+
+
+def down_flops(R: int, d: int, d_ff: int) -> int:
+    return 2 * R * d * d_ff
+
+
+def combine_bytes(T: int, k: int, d: int, out_bytes: int = 4) -> int:
+    """y_sorted (fp32) rows read, flat_to_sorted and gates read, y written."""
+    R = T * k
+    return R * d * 4 + R * 8 + T * d * out_bytes

@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE layer step on one MI355X: route -> permute -> grouped SwiGLU FFN -> combine.
+
+A step is one `moe_layer` call (every step of the path, one batch of T tokens) with all inputs
+resident in HBM. Prints ONE JSON line on stdout (progress goes to stderr):
+  value        layer tokens/s = T / (time per step), whole job (one GPU)
+  roofline     the dominant step (the grouped FFN) against its bound, from HIP-event timing of
+               that call on the stream it runs on, with algorithmic bytes / flops from
+               token_dispatch_expert_amd.traffic; traffic = counter-measured HBM bytes when a
+               profiles/ counter summary exists for the current kernel source, else null
+  cpu_baseline the fp64 oracle timed on the host cores (a bounded sample of the workload)
+  breakdown    per-call time and roofline fraction of every step
+
+Workloads (--config, default c2 = the decode-shape Qwen3-235B-like layer): c1..c5 as in
+synth.CONFIGS. Other modes: --calibrate-copy runs a plain device copy of known size, the
+reference for scaling the FETCH_SIZE / WRITE_SIZE counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 GPU; % MFMA peak (GEMM) and % HBM BW (permute/combine)"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+COPY_CAL_BYTES = 1 << 30          # --calibrate-copy moves exactly this many bytes each way
+FFN_SOURCE = os.path.join(ROOT, "token_dispatch_expert_amd", "csrc", "ffn.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per FFN call from a committed counter summary, if it matches this source."""
+    p = os.path.join(ROOT, "profiles", f"grouped_ffn_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        c = json.load(f)
+    if c.get("ffn_source_sha") != source_sha(FFN_SOURCE):
+        return None
+    return c.get("hbm_bytes_per_call")
+
+
+def calibrate_copy(steps: int) -> None:
+    import torch
+    n = COPY_CAL_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {COPY_CAL_BYTES} bytes x {steps}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library is one GPU's share of the layer and "
+              "has no multi-GPU path (the design notes describe how it would shard)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import token_dispatch_expert_amd as moe
+    from token_dispatch_expert_amd import traffic as tr
+    from token_dispatch_expert_amd.binding import layer_buffers
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        calibrate_copy(max(args.steps, 1))
+        return 0
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    T, E, k, d, d_ff = cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff
+    act_t = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    w_t = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3fn": torch.float8_e4m3fn}[cfg.w]
+
+    # ---- inputs (seeded, synthetic; every expert's weights exist, active or not)
+    t0 = time.time()
+    logits_np, x_np = synth.make_routing_inputs(cfg)
+    logits = torch.from_numpy(logits_np).to(dev)
+    if cfg.act == "f32":
+        x = torch.from_numpy(x_np).to(dev)
+    else:
+        x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    wshape = {"gate": (E, d_ff, d), "up": (E, d_ff, d), "down": (E, d, d_ff)}
+    W = {n: torch.empty(s, dtype=w_t, device=dev) for n, s in wshape.items()}
+    S = None
+    if cfg.w == "fp8_e4m3fn":
+        S = {"s_gate": torch.empty((E, d_ff // 128, d // 128), device=dev),
+             "s_up": torch.empty((E, d_ff // 128, d // 128), device=dev),
+             "s_down": torch.empty((E, d // 128, d_ff // 128), device=dev)}
+    host_w = {}
+    keep_host = not args.no_cpu_baseline
+    for e, w in synth.iter_expert_weights(cfg, range(E)):
+        for n in ("gate", "up", "down"):
+            src = torch.from_numpy(w[n].view(np.int16) if cfg.w == "bf16" else w[n])
+            W[n][e].copy_(src.to(dev).view(w_t))
+            if S is not None:
+                S["s_" + n][e].copy_(torch.from_numpy(w[n + "_scale"]).to(dev))
+        if keep_host:
+            host_w[e] = w
+        if e % 32 == 31:
+            log(f"weights: {e + 1}/{E} experts generated and uploaded")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s ({cfg.name}: T={T} d={d} E={E} k={k} d_ff={d_ff})")
+
+    out = layer_buffers(T, E, k, d, act_t, device=dev)
+    ws = moe.Workspace(moe.moe_layer_workspace_size(T, E, k, d, d_ff, act_t, w_t), device=dev)
+    skw = S or {}
+
+    def step():
+        moe.moe_layer(logits, x, W["gate"], W["up"], W["down"], k, out, ws, **skw)
+
+    # ---- warmup, then exactly K timed steps bracketed by synchronisation
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = T / (ms_per_step / 1e3)
+    log(f"layer: {ms_per_step * 1e3:.1f} us/step, {tokens_per_s:,.0f} tokens/s")
+
+    # ---- per-call timing with events on the stream the library launches on
+    counts = out["counts"].cpu().numpy()
+    active = int(np.count_nonzero(counts))
+    R = T * k
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    perm_ws = moe.Workspace(moe.moe_permute_workspace_size(T, E, k), device=dev)
+    ffn_ws = moe.Workspace(moe.moe_ffn_workspace_size(R, E, d, d_ff, act_t, w_t), device=dev)
+    acc = np.zeros(4)
+    reps = max(args.steps, 1)
+    for _ in range(reps):
+        ev[0].record(stream)
+        moe.moe_route(logits, k, out["topk_ids"], out["topk_gates"])
+        ev[1].record(stream)
+        moe.moe_permute(x, out["topk_ids"], E, out["counts"], out["offsets"], out["sorted_to_flat"],
+                        out["flat_to_sorted"], out["x_sorted"], perm_ws)
+        ev[2].record(stream)
+        moe.moe_grouped_ffn(out["x_sorted"], out["offsets"], W["gate"], W["up"], W["down"],
+                            out["y_sorted"], ffn_ws, **skw)
+        ev[3].record(stream)
+        moe.moe_combine(out["y_sorted"], out["flat_to_sorted"], out["topk_gates"], out["y"])
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    t_us = acc / reps * 1e3  # microseconds per call
+    a = 4 if cfg.act == "f32" else 2
+    wb = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[cfg.w]
+    sb = tr.fp8_scale_bytes(d, d_ff) if cfg.w == "fp8_e4m3fn" else 0
+    bytes_ = {
+        "route": tr.route_bytes(T, E, k),
+        "permute": tr.permute_bytes(T, E, k, d, a),
+        "grouped_ffn": tr.ffn_bytes(active, R, d, d_ff, wb, a, sb),
+        "combine": tr.combine_bytes(T, k, d),
+    }
+    flops = tr.ffn_flops(R, d, d_ff)
+    breakdown = {}
+    for i, name in enumerate(["route", "permute", "grouped_ffn", "combine"]):
+        gbps = bytes_[name] / (t_us[i] * 1e-6) / 1e9
+        breakdown[name] = {"us": round(float(t_us[i]), 2), "alg_bytes": int(bytes_[name]),
+                           "GB_per_s": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    mfma_peak = MFMA_PEAK_TFLOPS["fp32" if cfg.act == "f32" else "bf16"]
+    ffn_tflops = flops / (t_us[2] * 1e-6) / 1e12
+    breakdown["grouped_ffn"]["TFLOP_per_s"] = round(ffn_tflops, 2)
+    breakdown["grouped_ffn"]["mfma_frac"] = round(ffn_tflops / mfma_peak, 4)
+    # the FFN is HBM-bound when its intensity is below the ridge, MFMA-bound above it
+    intensity = flops / bytes_["grouped_ffn"]
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": round(bytes_["grouped_ffn"] / (t_us[2] * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = "moe_grouped_ffn (gate/up launch + down launch)"
+    roof["alg_bytes"] = int(bytes_["grouped_ffn"])
+    roof["alg_flops"] = int(flops)
+    roof["us"] = round(float(t_us[2]), 2)
+    roof["traffic"] = counter_traffic(cfg.name)
+    log(f"grouped_ffn: {t_us[2]:.1f} us, {roof['achieved']} {roof['unit']} = {roof['frac']:.1%} of peak")
+
+    # ---- CPU baseline: the fp64 oracle on the host cores
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        threads = max([i["num_threads"] for i in threadpool_info()] or [1])
+        if T <= 256:
+            Ts = T
+            sample = f"whole workload ({T} tokens), repeated until >= 10 s"
+        else:
+            Ts = 128
+            sample = f"first {Ts} of {T} tokens (same logits, x and weights), repeated until >= 10 s"
+        lg_s, x_s = logits_np[:Ts], x_np[:Ts]
+        log(f"cpu baseline: oracle on {Ts} tokens ...")
+        n_done, t_cpu = 0, 0.0
+        while t_cpu < 10.0 and n_done < 20:
+            tc = time.perf_counter()
+            oracle.layer(lg_s, x_s, cfg.act, lambda e: host_w[e], cfg.w, k)
+            t_cpu += time.perf_counter() - tc
+            n_done += 1
+        cpu = {"value": round(Ts * n_done / t_cpu, 2), "unit": "tokens/s", "cores": int(threads),
+               "kind": "oracle", "sample": sample, "seconds": round(t_cpu, 2)}
+        log(f"cpu baseline: {cpu['value']} tokens/s on {threads} threads")
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8_e4m3fn": "bf16 (fp8 e4m3fn weights)"}[cfg.w],
+        "data": "synthetic (seeded: Zipf-biased N(0,1) router logits, N(0,1) x, N(0,1/fan_in) weights)",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff,
+                   "activations": cfg.act, "weights": cfg.w, "zipf_s": cfg.zipf_s, "seed": cfg.seed,
+                   "active_experts": active, "max_rows_per_expert": int(counts.max())},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

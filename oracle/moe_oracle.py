@@ -27,6 +27,9 @@ oracle takes the readings listed below (each is also listed in the design notes)
   R5 fp8 weights: OCP e4m3fn codes times an fp32 scale per 128x128 block of the stored
      matrix, decoded exactly to fp64.
   R6 combine: fp64, summed in slot order j = 0..k-1; no token dropping.
+  R7 (optional, off by default) h_round="bf16": h is rounded to the nearest bf16 between the
+     two GEMMs, the rounding point of a bf16 implementation; tests use it as a second,
+     tighter comparison next to the plain fp64 one.
 Everything is fp64 after an exact decode of the stored inputs; there is no blocking, fusion
 or reordering beyond the steps above. Library primitives used as steps: numpy argmax (first
 occurrence of the maximum), fp64 matrix products (BLAS) and exp.
@@ -156,18 +159,31 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def round_bf16_value(v: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value of each fp64 value (8 significant bits, ties to even), as fp64.
+    Used only for the optional rounding-point mode below (finite, normal-range inputs)."""
+    m, e = np.frexp(np.asarray(v, dtype=np.float64))   # v = m * 2^e with 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def expert_ffn(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
-               return_h: bool = False):
+               return_h: bool = False, h_round: str | None = None):
     """SwiGLU of one expert over its rows X [n, d] (fp64); Wg, Wu stored [d_ff, d], Wd
-    stored [d, d_ff]."""
+    stored [d, d_ff]. h_round="bf16" rounds h to bf16 before the down projection (the
+    rounding point a bf16 implementation has between its two GEMMs); default: none."""
     G = X @ Wg.T
     U = X @ Wu.T
     h = silu(G) * U
+    if h_round == "bf16":
+        h = round_bf16_value(h)
+    elif h_round is not None:
+        raise ValueError(h_round)
     y = h @ Wd.T
     return (y, h) if return_h else y
 
 
-def ffn(x_sorted: np.ndarray, offsets: np.ndarray, expert_weights, return_h: bool = False):
+def ffn(x_sorted: np.ndarray, offsets: np.ndarray, expert_weights, return_h: bool = False,
+        h_round: str | None = None):
     """Grouped FFN: rows offsets[e]..offsets[e+1] go through expert e.
 
     x_sorted: fp64 [R, d]. expert_weights(e) -> (Wg, Wu, Wd) in fp64. Experts with no rows
@@ -181,7 +197,7 @@ def ffn(x_sorted: np.ndarray, offsets: np.ndarray, expert_weights, return_h: boo
         if a == b:
             continue
         Wg, Wu, Wd = expert_weights(e)
-        y_e, h_e = expert_ffn(x_sorted[a:b], Wg, Wu, Wd, return_h=True)
+        y_e, h_e = expert_ffn(x_sorted[a:b], Wg, Wu, Wd, return_h=True, h_round=h_round)
         y[a:b] = y_e
         if return_h:
             if h_all is None:
@@ -217,7 +233,8 @@ def make_weight_decoder(raw_weights, w_fmt: str):
     return dec
 
 
-def layer(logits, x, x_fmt: str, raw_weights, w_fmt: str, k: int, return_h: bool = False):
+def layer(logits, x, x_fmt: str, raw_weights, w_fmt: str, k: int, return_h: bool = False,
+          h_round: str | None = None):
     """The whole layer: route -> permute -> grouped FFN -> combine. Returns every
     intermediate."""
     T, E = np.asarray(logits).shape
@@ -227,9 +244,9 @@ def layer(logits, x, x_fmt: str, raw_weights, w_fmt: str, k: int, return_h: bool
     xs = decode_activations(x_sorted, x_fmt)
     dec = make_weight_decoder(raw_weights, w_fmt)
     if return_h:
-        y_sorted, h = ffn(xs, p["offsets"], dec, return_h=True)
+        y_sorted, h = ffn(xs, p["offsets"], dec, return_h=True, h_round=h_round)
     else:
-        y_sorted, h = ffn(xs, p["offsets"], dec), None
+        y_sorted, h = ffn(xs, p["offsets"], dec, h_round=h_round), None
     y = combine(y_sorted, p["flat_to_sorted"], gates)
     out = dict(topk_ids=ids, topk_gates=gates, x_sorted=x_sorted, y_sorted=y_sorted, y=y, **p)
     if return_h:
@@ -237,7 +254,8 @@ def layer(logits, x, x_fmt: str, raw_weights, w_fmt: str, k: int, return_h: bool
     return out
 
 
-def layer_tokens(tokens, topk_ids, topk_gates, x, x_fmt: str, raw_weights, w_fmt: str):
+def layer_tokens(tokens, topk_ids, topk_gates, x, x_fmt: str, raw_weights, w_fmt: str,
+                 h_round: str | None = None):
     """y[t] for the listed tokens only, from their own routing (used to check large layers
     on a sample: a token's output depends only on its own row, ids and gates). Returns
     (y [len(tokens), d], y_rows dict (t, j) -> that slot's expert output)."""
@@ -252,7 +270,7 @@ def layer_tokens(tokens, topk_ids, topk_gates, x, x_fmt: str, raw_weights, w_fmt
     rows = {}
     for e, items in sorted(by_expert.items()):
         Wg, Wu, Wd = dec(e)
-        Y = expert_ffn(X[[ti for ti, _ in items]], Wg, Wu, Wd)
+        Y = expert_ffn(X[[ti for ti, _ in items]], Wg, Wu, Wd, h_round=h_round)
         for (ti, j), yr in zip(items, Y):
             rows[(tokens[ti], j)] = yr
     y = np.zeros((len(tokens), X.shape[1]), dtype=np.float64)

@@ -115,9 +115,10 @@ def _e4m3fn_table() -> np.ndarray:
 _E4M3_MAG = _e4m3fn_table()
 
 
-def quantize_e4m3fn(v: np.ndarray) -> np.ndarray:
-    """Round fp32 values to OCP e4m3fn codes: nearest finite value, ties to the even code,
-    saturating at +-448."""
+def quantize_e4m3fn_table(v: np.ndarray) -> np.ndarray:
+    """Round fp32 values to OCP e4m3fn codes by search over the code table: nearest finite
+    value, ties to the even code, saturating at +-448 (slow; the cross-check of the fast
+    version below)."""
     a = np.abs(v.astype(np.float64))
     idx = np.searchsorted(_E4M3_MAG, a, side="left")
     hi = np.minimum(idx, 126)
@@ -130,22 +131,34 @@ def quantize_e4m3fn(v: np.ndarray) -> np.ndarray:
     return (code | (np.signbit(v).astype(np.uint8) << np.uint8(7))).astype(np.uint8)
 
 
+def quantize_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """Round fp32 values to OCP e4m3fn codes (round-to-nearest-even, saturating at +-448).
+
+    Normal range (|v| >= 2^-6): round the fp32 significand to 3 bits (add 0x7FFFF plus the
+    kept LSB, truncate) and rebias the exponent from 127 to 7. Subnormal range: multiples of
+    2^-9, rounded half-to-even. Results above 448 saturate to code 0x7E."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v)
+    u = a.view(np.uint32)
+    r = (u + np.uint32(0x7FFFF) + ((u >> np.uint32(20)) & np.uint32(1))) & np.uint32(0xFFF00000)
+    code_n = (((r >> np.uint32(23)).astype(np.int32) - 120) << 3) | ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
+    code_s = np.rint(a.astype(np.float64) * 512.0).astype(np.int32)
+    code = np.minimum(np.where(a < np.float32(2.0 ** -6), code_s, code_n), 126)
+    return code.astype(np.uint8) | (np.signbit(v).astype(np.uint8) << np.uint8(7))
+
+
 def quantize_blocks_e4m3fn(w: np.ndarray, block: int = 128):
     """Per-(block x block) quantisation of a stored fp32 matrix [N, K] -> (codes u8 [N, K],
-    scales f32 [ceil(N/block), ceil(K/block)])."""
+    scales f32 [ceil(N/block), ceil(K/block)]); scale = amax/448 (1.0 for an all-zero block)."""
     n, kk = w.shape
     nb, kb = -(-n // block), -(-kk // block)
-    scales = np.empty((nb, kb), dtype=np.float32)
-    codes = np.empty((n, kk), dtype=np.uint8)
-    for i in range(nb):
-        for j in range(kb):
-            blk = w[i * block:(i + 1) * block, j * block:(j + 1) * block]
-            amax = np.float32(np.max(np.abs(blk)))
-            s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
-            scales[i, j] = s
-            codes[i * block:(i + 1) * block, j * block:(j + 1) * block] = quantize_e4m3fn(
-                (blk / s).astype(np.float32))
-    return codes, scales
+    wp = np.zeros((nb * block, kb * block), dtype=np.float32)
+    wp[:n, :kk] = w
+    blocks = wp.reshape(nb, block, kb, block)
+    amax = np.max(np.abs(blocks), axis=(1, 3)).astype(np.float32)
+    scales = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = quantize_e4m3fn((blocks / scales[:, None, :, None]).astype(np.float32))
+    return np.ascontiguousarray(q.reshape(nb * block, kb * block)[:n, :kk]), scales
 
 
 # ----------------------------------------------------------------------------------------

@@ -1,0 +1,135 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol include/moe.h declares,
+and rejects invalid arguments with the documented status before making any HIP call (so these
+run without a GPU: every call below fails validation and enqueues nothing)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from token_dispatch_expert_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+# plausible-looking, suitably aligned device addresses; never dereferenced because every call
+# here fails host-side validation first
+P = 0x7F0000000000
+P2 = 0x7F0000100000
+P3 = 0x7F0000200000
+MIS = 0x7F0000000002  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|size_t|const char\s*\*)\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = B.library_path()
+    if not os.path.exists(path):
+        pytest.fail(f"{path} missing: run __graft_entry__.build()")
+    return B.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(B.ENTRY_POINTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)$", nm, re.M))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_string(s).decode()
+    assert lib.moe_status_string(99).decode() == "unknown status"
+
+
+def test_route_rejects_bad_arguments(lib):
+    r = lib.moe_route
+    assert r(None, 4, 8, 2, P, P2, None, None) == B.MOE_ERR_INVALID_ARG          # null logits
+    assert r(P, 4, 8, 9, P2, P3, None, None) == B.MOE_ERR_INVALID_ARG            # k > E
+    assert r(P, 4, 8, 0, P2, P3, None, None) == B.MOE_ERR_INVALID_ARG            # k = 0
+    assert r(P, -1, 8, 2, P2, P3, None, None) == B.MOE_ERR_INVALID_ARG           # T < 0
+    assert r(P, 4, 2048, 2, P2, P3, None, None) == B.MOE_ERR_UNSUPPORTED         # E > 1024
+    assert r(P, 4, 64, 33, P2, P3, None, None) == B.MOE_ERR_UNSUPPORTED          # k > 32
+    assert r(MIS, 4, 8, 2, P2, P3, None, None) == B.MOE_ERR_INVALID_ARG          # misaligned
+    assert r(P, 4, 8, 2, P2, P3, MIS, None) == B.MOE_ERR_INVALID_ARG             # misaligned counts
+    assert r(P, 1 << 30, 8, 4, P2, P3, None, None) == B.MOE_ERR_INVALID_ARG      # T*k overflows
+
+
+def test_permute_rejects_bad_arguments(lib):
+    pm = lib.moe_permute
+    T, E, k, d = 64, 8, 2, 128
+    ws = lib.moe_permute_workspace_size(T, E, k)
+    assert ws == 256  # one tile of 8 int32 histograms, rounded to 256 bytes
+    ok = [P, B.MOE_BF16, P2, T, E, k, d, P3, P3, P3, P3, P, P2, ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x", "dt", "ids", "T", "E", "k", "d", "counts", "offsets", "s2f", "f2s", "xs", "ws", "wsb", "s"]
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return pm(*a)
+
+    assert call(ws=None) == B.MOE_ERR_WORKSPACE
+    assert call(wsb=ws - 4) == B.MOE_ERR_WORKSPACE
+    assert call(dt=B.MOE_FP8_E4M3FN, ws=None) == B.MOE_ERR_UNSUPPORTED
+    assert call(d=12, ws=None) == B.MOE_ERR_UNSUPPORTED      # 24-byte rows are not 16-byte multiples
+    assert call(x=None, ws=None) == B.MOE_ERR_INVALID_ARG
+    assert call(xs=MIS, ws=None) == B.MOE_ERR_INVALID_ARG
+    assert call(k=9, ws=None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_ffn_rejects_bad_arguments(lib):
+    f = lib.moe_grouped_ffn
+    rows, E, d, d_ff = 128, 8, 256, 384
+    wsb = lib.moe_ffn_workspace_size(rows, E, d, d_ff, B.MOE_BF16, B.MOE_BF16)
+    assert wsb == rows * d_ff * 2
+    base = dict(x=P, act=B.MOE_BF16, off=P2, rows=rows, E=E, d=d, d_ff=d_ff, wg=P, wu=P2, wd=P3,
+                wdt=B.MOE_BF16, sg=None, su=None, sd=None, y=P, ws=P2, wsb=wsb, s=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+
+    assert call(act=B.MOE_F32, ws=None) == B.MOE_ERR_UNSUPPORTED                 # f32 act + bf16 w
+    assert call(act=B.MOE_FP8_E4M3FN, ws=None) == B.MOE_ERR_UNSUPPORTED
+    assert call(wdt=B.MOE_FP8_E4M3FN, d_ff=320, ws=None) == B.MOE_ERR_UNSUPPORTED  # d_ff not /128
+    assert call(wdt=B.MOE_FP8_E4M3FN, d_ff=512, ws=None) == B.MOE_ERR_INVALID_ARG  # scales missing
+    assert call(sg=P, ws=None) == B.MOE_ERR_INVALID_ARG                          # scales with bf16
+    assert call(d=100, ws=None) == B.MOE_ERR_UNSUPPORTED                         # d not /8
+    assert call(ws=None) == B.MOE_ERR_WORKSPACE
+    assert call(wsb=wsb - 1) == B.MOE_ERR_WORKSPACE
+    assert call(rows=-1, ws=None) == B.MOE_ERR_INVALID_ARG
+    assert call(wg=MIS, ws=None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_combine_and_layer_reject_bad_arguments(lib):
+    c = lib.moe_combine
+    assert c(P, P2, P3, 4, 2, 6, P, None) == B.MOE_ERR_UNSUPPORTED   # d not /4
+    assert c(None, P2, P3, 4, 2, 8, P, None) == B.MOE_ERR_INVALID_ARG
+    assert c(P, P2, P3, 4, 0, 8, P, None) == B.MOE_ERR_INVALID_ARG
+    T, E, k, d, d_ff = 16, 8, 2, 128, 256
+    need = lib.moe_layer_workspace_size(T, E, k, d, d_ff, B.MOE_BF16, B.MOE_BF16)
+    assert need == lib.moe_permute_workspace_size(T, E, k) + lib.moe_ffn_workspace_size(T * k, E, d, d_ff, B.MOE_BF16, B.MOE_BF16)
+    args = [P, P2, B.MOE_BF16, T, E, k, d, d_ff, P, P2, P3, B.MOE_BF16, None, None, None,
+            P, P2, P3, P, P2, P3, P, P2, P3, P, need - 16, None]
+    assert lib.moe_layer(*args) == B.MOE_ERR_WORKSPACE
+    args[-2] = need
+    args[2] = B.MOE_FP8_E4M3FN
+    assert lib.moe_layer(*args) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes(lib):
+    # one int32 per (tile of 1024 assignments, expert), rounded up to 256 bytes
+    assert lib.moe_permute_workspace_size(8192, 256, 8) == 64 * 256 * 4
+    assert lib.moe_permute_workspace_size(0, 256, 8) == 0
+    assert lib.moe_permute_workspace_size(5, 4, 9) == 0           # invalid -> 0
+    assert lib.moe_ffn_workspace_size(65536, 256, 7168, 2048, B.MOE_BF16, B.MOE_FP8_E4M3FN) == 65536 * 2048 * 2
+    assert lib.moe_ffn_workspace_size(128, 8, 128, 256, B.MOE_F32, B.MOE_F32) == 128 * 256 * 4

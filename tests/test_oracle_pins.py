@@ -256,11 +256,20 @@ def check_bf16_layer_decodes_inputs():
     assert oracle.rel_max_err(out["y"], ref) < 1e-12
 
 
+def check_bf16_value_rounding():
+    # on fp32-representable inputs, rounding fp64 straight to bf16 must equal torch's fp32->bf16
+    rng = np.random.default_rng(12)
+    v = np.concatenate([rng.standard_normal(50000) * 3, [1.00390625, 1.01171875, -2.0 ** -20 * 1.00390625]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16_value(v.astype(np.float64)), ref)
+
+
 CHECKS = [
     check_decode_bf16, check_decode_e4m3fn, check_route_vs_stable_argsort,
     check_route_special_cases, check_permute_vs_library, check_golden_load_example,
     check_golden_volume_example, check_swiglu_closed_form, check_brute_force_layer,
     check_identity_experts_and_gather, check_fp8_dequant_blocks, check_bf16_layer_decodes_inputs,
+    check_bf16_value_rounding,
 ]
 
 

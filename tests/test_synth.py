@@ -23,6 +23,7 @@ def test_e4m3fn_quantizer_matches_torch():
     got = synth.quantize_e4m3fn(v)
     # torch keeps the sign of a zero result; so do we
     assert np.array_equal(got, ref)
+    assert np.array_equal(synth.quantize_e4m3fn_table(v), ref)
 
 
 def test_block_quantisation_roundtrip_error():

@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP kernels and the C ABI host code (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------
+// vector types used for MFMA operands and 16-byte memory moves
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Permutation tiles: flat assignments are processed in tiles of this many entries.
+constexpr int kPermuteTile = 1024;
+
+// Grouped-FFN streaming kernel geometry (see ffn.hip).
+constexpr int kStreamWaves = 4;     // waves per workgroup; they split the contraction axis
+constexpr int kStreamMFrags = 4;    // 16-row MFMA fragments per item -> up to 64 rows
+constexpr int kStreamRows = 16 * kStreamMFrags;
+
+struct DeviceInfo {
+  int device = -1;
+  int num_cus = 0;
+};
+
+// Queried once per device, cached (mutex-guarded) in api.cpp.
+hipError_t device_info(DeviceInfo* out);
+
+// ---------------------------------------------------------------------------------------
+// launchers (each enqueues on `stream` and returns the launch status)
+// ---------------------------------------------------------------------------------------
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t value, hipStream_t stream);
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
+                        int32_t* counts, hipStream_t stream);
+
+// workspace: n_tiles * E int32 (per-tile histograms, then per-tile bases)
+size_t permute_workspace_ints(int T, int E, int k);
+hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int T, int E, int k,
+                          int d, int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat,
+                          int32_t* flat_to_sorted, void* x_sorted, int32_t* ws,
+                          hipStream_t stream);
+
+struct FfnArgs {
+  const void* x_sorted;
+  moe_dtype_t act;
+  const int32_t* offsets;
+  int rows, E, d, d_ff;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  moe_dtype_t wdt;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  float* y_sorted;
+  void* h;  // [rows, d_ff] in act dtype (workspace)
+};
+size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt);
+hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream);
+
+hipError_t launch_combine(const float* y_sorted, const int32_t* flat_to_sorted,
+                          const float* gates, int T, int k, int d, float* y, hipStream_t stream);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe

@@ -1,0 +1,162 @@
+// Expert sort of the T*k assignments: histogram, exclusive scan, stable scatter, row copy.
+//
+// Operation: "Expert Parallelism" tutorial page, section 4, dispatch (sort by destination
+// expert, count, every expert ends up with a contiguous block of rows) and section 9 (an
+// unsorted batch means divergent, uncoalesced work). Reading taken: the sort is stable in
+// the flat index i = t*k + j, so within an expert rows appear in token order and the
+// permutation is unique (the k experts of one token are distinct).
+//
+// Four launches, none using float atomics, all deterministic:
+//   hist : one workgroup per tile of kPermuteTile flat entries; LDS histogram -> ws[tile][e]
+//   scan : one workgroup; per expert an exclusive prefix over tiles, then counts, the
+//          exclusive scan over experts (offsets) and per-tile bases ws[tile][e]
+//   rank : one wavefront per tile walks its entries in flat order, 64 at a time; lanes with
+//          the same expert find each other with ballots over the expert id's bits, so a
+//          lane's rank among equal keys is a popcount of lower lanes; the group's last lane
+//          advances the running base in LDS. Writes both index maps.
+//   copy : one workgroup per token reads x[t] once in 16-byte vectors and stores it to its
+//          k sorted rows.
+#include "moe_internal.h"
+
+namespace moe {
+
+size_t permute_workspace_ints(int T, int E, int k) {
+  const size_t R = (size_t)T * (size_t)k;
+  const size_t tiles = (R + kPermuteTile - 1) / kPermuteTile;
+  return tiles * (size_t)E;
+}
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ ids, int R,
+                                                           int E, int32_t* __restrict__ ws) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kPermuteTile;
+  const int end = min(base + kPermuteTile, R);
+  for (int i = base + threadIdx.x; i < end; i += blockDim.x)
+    atomicAdd(&hist[clamp_expert(ids[i], E)], 1);
+  __syncthreads();
+  int32_t* out = ws + (size_t)blockIdx.x * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
+}
+
+constexpr int kScanThreads = 1024;  // >= MOE_MAX_EXPERTS
+
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ ws,
+                                                                    int n_tiles, int E, int R,
+                                                                    int32_t* __restrict__ counts,
+                                                                    int32_t* __restrict__ offsets) {
+  __shared__ int32_t sc[kScanThreads];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    // exclusive prefix over tiles (batches of independent loads hide latency)
+    constexpr int B = 16;
+    for (int t0 = 0; t0 < n_tiles; t0 += B) {
+      int h[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) h[u] = (t0 + u < n_tiles) ? ws[(size_t)(t0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (t0 + u < n_tiles) {
+          ws[(size_t)(t0 + u) * E + e] = total;
+          total += h[u];
+        }
+      }
+    }
+    counts[e] = total;
+  }
+  sc[threadIdx.x] = total;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+    __syncthreads();
+    sc[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const int excl = sc[threadIdx.x] - total;
+  if (e < E) {
+    offsets[e] = excl;
+    for (int t = 0; t < n_tiles; ++t) ws[(size_t)t * E + e] += excl;
+  }
+  if (threadIdx.x == 0) offsets[E] = R;
+}
+
+__global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __restrict__ ids,
+                                                             int R, int E, int nbits,
+                                                             const int32_t* __restrict__ ws,
+                                                             int32_t* __restrict__ s2f,
+                                                             int32_t* __restrict__ f2s) {
+  extern __shared__ int32_t run[];
+  const int lane = threadIdx.x;
+  const int32_t* bases = ws + (size_t)blockIdx.x * E;
+  for (int e = lane; e < E; e += kWave) run[e] = bases[e];
+  __syncthreads();
+  const int base = blockIdx.x * kPermuteTile;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int c = 0; c < kPermuteTile; c += kWave) {
+    const int i = base + c + lane;
+    const bool valid = i < R;
+    const int e = valid ? clamp_expert(ids[i], E) : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    if (valid) {
+      const int pos = run[e] + __popcll(same & lower);
+      s2f[pos] = i;
+      f2s[i] = pos;
+    }
+    __syncthreads();
+    // the highest lane of each group of equal experts advances that expert's base
+    if (valid && (63 - __clzll(same)) == lane) run[e] += __popcll(same);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restrict__ x, int k,
+                                                           int vec_per_row,
+                                                           const int32_t* __restrict__ f2s,
+                                                           uint4* __restrict__ xs) {
+  const int t = blockIdx.x;
+  const int32_t* pos = f2s + (size_t)t * k;
+  const uint4* src = x + (size_t)t * vec_per_row;
+  for (int v = threadIdx.x; v < vec_per_row; v += blockDim.x) {
+    const uint4 val = src[v];
+    for (int j = 0; j < k; ++j) xs[(size_t)pos[j] * vec_per_row + v] = val;
+  }
+}
+
+hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int T, int E, int k,
+                          int d, int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat,
+                          int32_t* flat_to_sorted, void* x_sorted, int32_t* ws,
+                          hipStream_t stream) {
+  const int R = T * k;
+  const int n_tiles = (R + kPermuteTile - 1) / kPermuteTile;
+  const size_t lds = (size_t)E * sizeof(int32_t);
+  if (n_tiles > 0) {
+    permute_hist_kernel<<<n_tiles, 256, lds, stream>>>(ids, R, E, ws);
+    hipError_t st = hipGetLastError();
+    if (st != hipSuccess) return st;
+  }
+  permute_scan_kernel<<<1, kScanThreads, 0, stream>>>(ws, n_tiles, E, R, counts, offsets);
+  hipError_t st = hipGetLastError();
+  if (st != hipSuccess || n_tiles == 0) return st;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  permute_rank_kernel<<<n_tiles, kWave, lds, stream>>>(ids, R, E, nbits, ws, sorted_to_flat,
+                                                        flat_to_sorted);
+  st = hipGetLastError();
+  if (st != hipSuccess) return st;
+  const int vpr = d * elem_bytes / 16;
+  const int threads = vpr >= 256 ? 256 : ((vpr + kWave - 1) / kWave) * kWave;
+  permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,
+                                                 flat_to_sorted, static_cast<uint4*>(x_sorted));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -102,10 +102,19 @@ struct StreamArgs {
   int max_rows;         // experts with more rows are left to another kernel
 };
 
-constexpr int kMF = 2;                 // 16-row fragments per item
+constexpr int kMF = 1;                 // 16-row fragments per item
+constexpr int kStreamMaxRows = 16;     // larger experts use the tiled kernel (bf16 path)
 constexpr int kItemRows = 16 * kMF;    // rows per item
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not wait for the
+// wave's outstanding global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Rows [a, b) of expert e, with the offsets clamped into [0, rows] and made non-decreasing so
 // that corrupt offsets can never address memory out of bounds.
@@ -117,8 +126,11 @@ __device__ __forceinline__ void expert_rows(const int32_t* offsets, int e, int r
 }
 
 // Build the item prefix over experts in LDS: pre[e] = first item of expert e; pre[E] = total.
+// offs (optional) receives the clamped row offsets of every expert, offs[0..E].
 __device__ void build_item_prefix(int32_t* pre, int32_t* scratch, const int32_t* offsets, int E,
-                                  int rows, int max_rows, int items_per_group) {
+                                  int rows, int max_rows, int items_per_group,
+                                  int32_t* offs = nullptr, int min_rows = 0,
+                                  int rows_per_group = kItemRows) {
   const int tid = threadIdx.x;
   const int per = (E + blockDim.x - 1) / blockDim.x;  // experts per thread (<= 4)
   int local[4];
@@ -131,8 +143,13 @@ __device__ void build_item_prefix(int32_t* pre, int32_t* scratch, const int32_t*
       int a, b;
       expert_rows(offsets, e, rows, a, b);
       n = b - a;
+      if (offs) {
+        offs[e] = a;
+        if (e == E - 1) offs[E] = b;
+      }
     }
-    local[i] = (n > 0 && n <= max_rows) ? ((n + kItemRows - 1) / kItemRows) * items_per_group : 0;
+    local[i] = (n > min_rows && n <= max_rows)
+                   ? ((n + rows_per_group - 1) / rows_per_group) * items_per_group : 0;
     sum += local[i];
   }
   scratch[tid] = sum;
@@ -156,170 +173,204 @@ __device__ void build_item_prefix(int32_t* pre, int32_t* scratch, const int32_t*
   __syncthreads();
 }
 
-// MATS = 2 for the gate/up pass (gate and up share an item), 1 for the down pass.
-// SPB = 32-long MFMA steps per contraction block (a wave's unit of work and of prefetch).
+// A workgroup of 4 waves streams one item at a time: (expert e, 32-row group, NF*16 columns
+// of each of the MATS matrices). The waves split the item's contraction axis into 4 ranges;
+// each wave's blocks (KB = SPB*32 elements) form one continuous stream across the items of
+// its workgroup: a ring of NBUF register slots keeps NBUF-1 blocks of loads in flight ahead
+// of the block feeding the MFMAs, across item boundaries. Every slot load is issued
+// unconditionally (addresses clamped in-bounds, out-of-range data discarded), which keeps the
+// compiler's memory-counter waits exact. At the end of an item the waves reduce their partial
+// tiles through LDS in a fixed order (deterministic) and all 256 threads run the epilogue.
 template <int AF, int WF, int MATS, int NF, int SPB>
+struct Slot {
+  Raw<AF> a[kMF][SPB];
+  Raw<WF> b[MATS][NF][SPB];
+  int e, r_begin, nrows, n0, kb;
+  bool valid, last, dummy;
+};
+
+template <int AF, int WF, int MATS, int NF, int SPB, int NBUF>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamArgs p) {
-  constexpr int kCols = MATS * NF * 16;  // columns of the partial tile
-  constexpr int kLdsStride = kCols + 4;
-  constexpr int KB = SPB * 32;           // contraction block
+  constexpr int KB = SPB * 32;
+  constexpr int kCols = MATS * NF * 16;
+  constexpr int kStride = kCols + 4;
   extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* pre = reinterpret_cast<int32_t*>(smem);                               // E+1
-  int32_t* scan_tmp = pre + ((p.E + 1 + 3) & ~3);                                // 256
-  float* red = reinterpret_cast<float*>(scan_tmp + 256);                         // 4*32*stride
+  const int Epad = (p.E + 1 + 3) & ~3;
+  int32_t* pre = reinterpret_cast<int32_t*>(smem);         // E+1
+  int32_t* offs = pre + Epad;                               // E+1 clamped row offsets
+  int32_t* scan_tmp = offs + Epad;                          // 256
+  float* red = reinterpret_cast<float*>(scan_tmp + 256);    // [4][kItemRows][kStride]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NB = (p.N + NF * 16 - 1) / (NF * 16);
-  build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, p.max_rows, NB);
-  const int total = pre[p.E];
+  build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, p.max_rows, NB, offs);
+  const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
+  if ((int)blockIdx.x >= total) return;  // uniform per workgroup
   const int nkb = (p.K + KB - 1) / KB;
-  const int kb_begin = (nkb * wave) / kStreamWaves;
-  const int kb_end = (nkb * (wave + 1)) / kStreamWaves;
+  // this wave's contraction blocks [kb0, kb0 + nblk); a wave with no blocks (tiny K) runs one
+  // masked dummy block per item so that it still meets every item's barrier
+  const int per = (nkb + kStreamWaves - 1) / kStreamWaves;
+  const int kb0 = min(wave * per, nkb);
+  const int kb1 = min(kb0 + per, nkb);
+  const bool dummy = kb0 >= kb1;
+  const int nblk = dummy ? 1 : kb1 - kb0;
   const int nNB128 = (p.N + 127) / 128, nKB128 = (p.K + 127) / 128;
-  const size_t wstride = (size_t)p.N * p.K;  // elements per expert matrix
+  const size_t wstride = (size_t)p.N * p.K;
+  const int kl = (lane >> 4) * 8;
+  const void* Wm[2] = {p.W1, p.W2};
+  const float* Sm[2] = {p.S1, p.S2};
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // expert owning this item: largest e with pre[e] <= item
+  // load cursor (wave-uniform; readfirstlane keeps it in scalar registers)
+  int l_item = blockIdx.x, l_j = 0;
+  int l_e = 0, l_rb = 0, l_nr = 0, l_n0 = 0;
+  auto decode = [&](int item) {
     int lo = 0, hi = p.E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= item) lo = mid; else hi = mid - 1;
+      if (__builtin_amdgcn_readfirstlane(pre[mid]) <= item) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int local = item - pre[e];
-    const int mg = local / NB, nb = local % NB;
-    int e_begin, e_end;
-    expert_rows(p.offsets, e, p.rows, e_begin, e_end);
-    const int r_begin = e_begin + mg * kItemRows;
-    const int r_end = min(r_begin + kItemRows, e_end);
-    const int nmf = (r_end - r_begin + 15) / 16;
-    const int n0 = nb * NF * 16;
+    const int eb = __builtin_amdgcn_readfirstlane(offs[lo]);
+    const int ee = __builtin_amdgcn_readfirstlane(offs[lo + 1]);
+    const int local = item - __builtin_amdgcn_readfirstlane(pre[lo]);
+    const int mg = local / NB;
+    l_e = lo;
+    l_rb = eb + mg * kItemRows;
+    l_nr = min(kItemRows, ee - l_rb);
+    l_n0 = (local % NB) * NF * 16;
+  };
+  decode(l_item);
 
-    // per-lane operand addresses (clamped in-bounds; masked on store)
-    size_t a_row[kMF];
-#pragma unroll
-    for (int mf = 0; mf < kMF; ++mf) a_row[mf] = (size_t)min(r_begin + mf * 16 + (lane & 15), r_end - 1) * p.K;
+  Slot<AF, WF, MATS, NF, SPB> slot[NBUF];
+
+  auto issue = [&](Slot<AF, WF, MATS, NF, SPB>& s) {
+    const bool valid = l_item < total;
+    const int kb = dummy ? nkb - 1 : kb0 + l_j;
+    s.valid = valid;
+    s.e = l_e; s.r_begin = l_rb; s.nrows = l_nr; s.n0 = l_n0; s.kb = kb;
+    s.last = l_j == nblk - 1;
+    s.dummy = dummy;
     size_t b_row[NF];
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf) b_row[nf] = (size_t)e * wstride + (size_t)min(n0 + nf * 16 + (lane & 15), p.N - 1) * p.K;
-    const void* Wm[2] = {p.W1, p.W2};
-    const float* Sm[2] = {p.S1, p.S2};
-    const int kl = (lane >> 4) * 8;
-
-    f32x4 acc[kMF][MATS][NF];
+    for (int nf = 0; nf < NF; ++nf)
+      b_row[nf] = (size_t)l_e * wstride + (size_t)min(l_n0 + nf * 16 + (lane & 15), p.N - 1) * p.K;
+    size_t a_row[kMF];
 #pragma unroll
     for (int mf = 0; mf < kMF; ++mf)
+      a_row[mf] = (size_t)(l_rb + min(mf * 16 + (lane & 15), l_nr - 1)) * p.K;
+#pragma unroll
+    for (int st = 0; st < SPB; ++st) {
+      const int k = kb * KB + st * 32 + kl;
+      const int kc = k < p.K ? k : p.K - 8;
 #pragma unroll
       for (int m = 0; m < MATS; ++m)
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) acc[mf][m][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Raw<AF> a_cur[kMF][SPB], a_nxt[kMF][SPB];
-    Raw<WF> b_cur[MATS][NF][SPB], b_nxt[MATS][NF][SPB];
-
-    auto load_block = [&](int kb, Raw<AF> (&a)[kMF][SPB], Raw<WF> (&b)[MATS][NF][SPB]) {
+        for (int nf = 0; nf < NF; ++nf) load_frag<WF>(s.b[m][nf][st], Wm[m], b_row[nf] + kc, true);
 #pragma unroll
-      for (int s = 0; s < SPB; ++s) {
-        const int k = kb * KB + s * 32 + kl;
-        const bool kok = k < p.K;
+      for (int mf = 0; mf < kMF; ++mf) load_frag<AF>(s.a[mf][st], p.X, a_row[mf] + kc, true);
+    }
+    if (valid && ++l_j == nblk) {
+      l_j = 0;
+      l_item += gridDim.x;
+      if (l_item < total) decode(l_item);
+    }
+  };
+
+  f32x4 acc[kMF][MATS][NF];
+#pragma unroll
+  for (int mf = 0; mf < kMF; ++mf)
+#pragma unroll
+    for (int m = 0; m < MATS; ++m)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) acc[mf][m][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](Slot<AF, WF, MATS, NF, SPB>& s) {
+    if (s.dummy) return;
+    const int nmf = (s.nrows + 15) / 16;
+    // contraction tail (K not a multiple of the block): lanes past K loaded a clamped
+    // in-bounds address; zero their activation operand now that the data has arrived
+    if ((s.kb + 1) * KB > p.K) {
+#pragma unroll
+      for (int st = 0; st < SPB; ++st)
+        if (s.kb * KB + st * 32 + kl >= p.K)
+#pragma unroll
+          for (int mf = 0; mf < kMF; ++mf) s.a[mf][st] = Raw<AF>{};
+    }
+    if constexpr (WF == kFP8) {
+      f32x4 part[kMF][MATS][NF];
+#pragma unroll
+      for (int mf = 0; mf < kMF; ++mf)
 #pragma unroll
         for (int m = 0; m < MATS; ++m)
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf) load_frag<WF>(b[m][nf][s], Wm[m], b_row[nf] + k, kok);
+          for (int nf = 0; nf < NF; ++nf) part[mf][m][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mf = 0; mf < kMF; ++mf) load_frag<AF>(a[mf][s], p.X, a_row[mf] + k, kok && mf < nmf);
-      }
-    };
-
-    if (kb_begin < kb_end) load_block(kb_begin, a_cur, b_cur);
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-      if (kb + 1 < kb_end) load_block(kb + 1, a_nxt, b_nxt);
-      if constexpr (WF == kFP8) {
-        f32x4 part[kMF][MATS][NF];
+      for (int st = 0; st < SPB; ++st)
 #pragma unroll
         for (int mf = 0; mf < kMF; ++mf)
+          if (mf < nmf)
 #pragma unroll
-          for (int m = 0; m < MATS; ++m)
+            for (int m = 0; m < MATS; ++m)
 #pragma unroll
-            for (int nf = 0; nf < NF; ++nf) part[mf][m][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+              for (int nf = 0; nf < NF; ++nf) mma<AF, WF>(part[mf][m][nf], s.a[mf][st], s.b[m][nf][st]);
 #pragma unroll
-        for (int s = 0; s < SPB; ++s)
+      for (int m = 0; m < MATS; ++m)
 #pragma unroll
-          for (int mf = 0; mf < kMF; ++mf)
-            if (mf < nmf)
-#pragma unroll
-              for (int m = 0; m < MATS; ++m)
-#pragma unroll
-                for (int nf = 0; nf < NF; ++nf) mma<AF, WF>(part[mf][m][nf], a_cur[mf][s], b_cur[m][nf][s]);
-#pragma unroll
-        for (int m = 0; m < MATS; ++m)
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            const int nbs = (n0 + nf * 16) / 128;
-            const float sc = Sm[m][((size_t)e * nNB128 + min(nbs, nNB128 - 1)) * nKB128 + (kb * KB) / 128];
-#pragma unroll
-            for (int mf = 0; mf < kMF; ++mf)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[mf][m][nf][j] = fmaf(sc, part[mf][m][nf][j], acc[mf][m][nf][j]);
-          }
-      } else {
-#pragma unroll
-        for (int s = 0; s < SPB; ++s)
+        for (int nf = 0; nf < NF; ++nf) {
+          const int nbs = min((s.n0 + nf * 16) / 128, nNB128 - 1);
+          const float sc = Sm[m][((size_t)s.e * nNB128 + nbs) * nKB128 + (s.kb * KB) / 128];
 #pragma unroll
           for (int mf = 0; mf < kMF; ++mf)
-            if (mf < nmf)
 #pragma unroll
-              for (int m = 0; m < MATS; ++m)
-#pragma unroll
-                for (int nf = 0; nf < NF; ++nf) mma<AF, WF>(acc[mf][m][nf], a_cur[mf][s], b_cur[m][nf][s]);
-      }
-      if (kb + 1 < kb_end) {
-#pragma unroll
-        for (int s = 0; s < SPB; ++s) {
-#pragma unroll
-          for (int mf = 0; mf < kMF; ++mf) a_cur[mf][s] = a_nxt[mf][s];
-#pragma unroll
-          for (int m = 0; m < MATS; ++m)
-#pragma unroll
-            for (int nf = 0; nf < NF; ++nf) b_cur[m][nf][s] = b_nxt[m][nf][s];
+            for (int j = 0; j < 4; ++j) acc[mf][m][nf][j] = fmaf(sc, part[mf][m][nf][j], acc[mf][m][nf][j]);
         }
-      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < SPB; ++st)
+#pragma unroll
+        for (int mf = 0; mf < kMF; ++mf)
+          if (mf < nmf)
+#pragma unroll
+            for (int m = 0; m < MATS; ++m)
+#pragma unroll
+              for (int nf = 0; nf < NF; ++nf) mma<AF, WF>(acc[mf][m][nf], s.a[mf][st], s.b[m][nf][st]);
     }
+  };
 
-    // partial tiles -> LDS: lane holds rows (lane/16)*4 + j, column lane%16 of each fragment
-    float* mine = red + (size_t)wave * kItemRows * kLdsStride;
+  // end of an item: partial tiles -> LDS (lane holds rows (lane/16)*4 + j, column lane%16 of
+  // each fragment), barrier, fixed-order reduction + epilogue by all threads, barrier
+  auto finish = [&](const Slot<AF, WF, MATS, NF, SPB>& s) {
+    float* mine = red + (size_t)wave * kItemRows * kStride;
 #pragma unroll
     for (int mf = 0; mf < kMF; ++mf)
 #pragma unroll
       for (int m = 0; m < MATS; ++m)
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
+        for (int nf = 0; nf < NF; ++nf) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            mine[(mf * 16 + (lane >> 4) * 4 + j) * kLdsStride + m * NF * 16 + nf * 16 + (lane & 15)] = acc[mf][m][nf][j];
-    __syncthreads();
-
-    const int nrows = r_end - r_begin;
+            mine[(mf * 16 + (lane >> 4) * 4 + j) * kStride + m * NF * 16 + nf * 16 + (lane & 15)] = acc[mf][m][nf][j];
+          acc[mf][m][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    lds_barrier();
     if constexpr (MATS == 2) {
-      // gate/up epilogue: h = silu(gate) * up, 8 (bf16) or 4 (fp32) columns per task
       constexpr int G = (AF == kF32) ? 4 : 8;
       constexpr int groups = NF * 16 / G;
       for (int task = threadIdx.x; task < kItemRows * groups; task += blockDim.x) {
         const int r = task / groups, c0 = (task % groups) * G;
-        if (r >= nrows || n0 + c0 >= p.N) continue;
+        if (r >= s.nrows || s.n0 + c0 >= p.N) continue;
         float hv[G];
 #pragma unroll
         for (int c = 0; c < G; ++c) {
           float g = 0.f, u = 0.f;
 #pragma unroll
           for (int w = 0; w < kStreamWaves; ++w) {
-            g += red[((size_t)w * kItemRows + r) * kLdsStride + c0 + c];
-            u += red[((size_t)w * kItemRows + r) * kLdsStride + NF * 16 + c0 + c];
+            g += red[((size_t)w * kItemRows + r) * kStride + c0 + c];
+            u += red[((size_t)w * kItemRows + r) * kStride + NF * 16 + c0 + c];
           }
           hv[c] = silu(g) * u;
         }
-        const size_t o = (size_t)(r_begin + r) * p.N + n0 + c0;
+        const size_t o = (size_t)(s.r_begin + r) * p.N + s.n0 + c0;
         if constexpr (AF == kF32) {
           *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(hv[0], hv[1], hv[2], hv[3]);
         } else {
@@ -335,30 +386,497 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamArgs p) {
       constexpr int groups = NF * 16 / 4;
       for (int task = threadIdx.x; task < kItemRows * groups; task += blockDim.x) {
         const int r = task / groups, c0 = (task % groups) * 4;
-        if (r >= nrows || n0 + c0 >= p.N) continue;
+        if (r >= s.nrows || s.n0 + c0 >= p.N) continue;
         float v[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          float s = 0.f;
+          float sum = 0.f;
 #pragma unroll
-          for (int w = 0; w < kStreamWaves; ++w) s += red[((size_t)w * kItemRows + r) * kLdsStride + c0 + c];
-          v[c] = s;
+          for (int w = 0; w < kStreamWaves; ++w) sum += red[((size_t)w * kItemRows + r) * kStride + c0 + c];
+          v[c] = sum;
         }
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)(r_begin + r) * p.N + n0 + c0) =
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)(s.r_begin + r) * p.N + s.n0 + c0) =
             make_float4(v[0], v[1], v[2], v[3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) issue(slot[i]);
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      issue(slot[(i + NBUF - 1) % NBUF]);
+      if (!slot[i].valid) return;  // the same for every wave of the workgroup
+      compute(slot[i]);
+      if (slot[i].last) finish(slot[i]);
+    }
   }
 }
 
-template <int AF, int WF, int MATS, int NF, int SPB>
+template <int AF, int WF, int MATS, int NF, int SPB, int NBUF>
 static hipError_t launch_stream(const StreamArgs& p, const DeviceInfo& dev, hipStream_t stream) {
   constexpr int kCols = MATS * NF * 16;
-  const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 + 256) * sizeof(int32_t) +
+  const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + 256) * sizeof(int32_t) +
                      (size_t)kStreamWaves * kItemRows * (kCols + 4) * sizeof(float);
   const int grid = dev.num_cus * 2;
-  ffn_stream_kernel<AF, WF, MATS, NF, SPB><<<grid, 256, lds, stream>>>(p);
+  ffn_stream_kernel<AF, WF, MATS, NF, SPB, NBUF><<<grid, 256, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Tiled kernel for experts with many rows (the GEMM-tile regime): a workgroup of 4 waves
+// computes a (2*WM)-row x (2*WN)-column output tile over the whole contraction axis in
+// 64-wide steps. For the gate/up pass the tile's columns are WN gate and the same WN up
+// columns of h. Operand tiles are staged in LDS (double-buffered: the next step's global
+// loads are in flight while the MFMAs consume the current one), so each weight tile is read
+// from memory once per 2*WM rows of its expert and each activation tile once per tile of
+// columns. The waves split the tile 2 x 2; wave (wm, wn) owns rows wm*WM..+WM-1 and, in the
+// gate/up pass, gate and up columns c0 + wn*WN/2.. (so SwiGLU is applied in registers).
+// Two shapes are instantiated: 64 x 64 per wave for decode-sized batches and 128 x 128 per
+// wave (256 fp32 accumulators per lane, in AGPRs) for prefill, where a larger tile halves
+// the LDS and L2 traffic per MFMA.
+// LDS tiles hold 64-wide rows of bf16 (128 bytes = 8 chunks of 16 bytes) with an XOR
+// swizzle: chunk c of row r is stored at chunk c ^ ((r >> 1) & 7). A 16-byte fragment load
+// reads one chunk from each of 16 consecutive rows, and the staging store writes the 8 chunks
+// of two consecutive rows per 16 lanes; with the swizzle both touch all 64 banks exactly once.
+constexpr int kTK = 64;
+constexpr int kLdsRow = kTK;
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kLdsRow + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+struct TiledArgs {
+  const void* X;
+  const void* W1;
+  const void* W2;
+  const float* S1;
+  const float* S2;
+  void* out;
+  const int32_t* offsets;
+  int E, K, N, rows;
+  int min_rows;  // experts with at most this many rows are left to the streaming kernel
+};
+
+template <int WF, bool GATED, int WM, int WN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_kernel(TiledArgs p) {
+  constexpr int NTH = 64 * WGM * WGN;                        // threads per workgroup
+  constexpr int TM = WGM * WM, TN = WGN * WN;
+  constexpr int MF = WM / 16, NF = WN / 16;
+  constexpr int ACH = TM * 8 / NTH;                         // 16-byte A chunks per thread
+  constexpr int BCH = (WF == kFP8) ? TN * 4 / NTH : TN * 8 / NTH;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Epad = (p.E + 1 + 3) & ~3;
+  int32_t* pre = reinterpret_cast<int32_t*>(smem);
+  int32_t* offs = pre + Epad;
+  int32_t* scan_tmp = offs + Epad;
+  __bf16* lds_a = reinterpret_cast<__bf16*>(scan_tmp + NTH);   // [2][TM][kLdsRow]
+  __bf16* lds_b = lds_a + 2 * TM * kLdsRow;                     // [2][TN][kLdsRow]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  constexpr int cols_per_tile = GATED ? TN / 2 : TN;
+  const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
+  build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, 0x7fffffff, NT, offs, p.min_rows, TM);
+  const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
+  const int nkb = p.K / kTK;  // K is a multiple of kTK on this path
+  const int nNB128 = (p.N + 127) / 128, nKB128 = (p.K + 127) / 128;
+  const size_t wstride = (size_t)p.N * p.K;
+  const int kl = (lane >> 4) * 8;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = p.E;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(pre[mid]) <= item) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int local = item - __builtin_amdgcn_readfirstlane(pre[e]);
+    // Tile order within an expert: groups of kGroupM row tiles, column tiles outer and row
+    // tiles inner within a group. Workgroups are dealt to the 8 XCDs round-robin, so the 32
+    // concurrent workgroups of one XCD cover 4 row tiles x 8 column tiles of the same expert
+    // and share both operands in that XCD's L2.
+    constexpr int kGroupM = 4;
+    const int ebeg = __builtin_amdgcn_readfirstlane(offs[e]);
+    const int MT = (__builtin_amdgcn_readfirstlane(offs[e + 1]) - ebeg + TM - 1) / TM;
+    const int g = local / (kGroupM * NT);
+    const int gm = min(kGroupM, MT - g * kGroupM);
+    const int j = local - g * kGroupM * NT;
+    const int nt = j / gm;
+    const int mt = g * kGroupM + j % gm;
+    const int r0 = ebeg + mt * TM;
+    const int nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
+    const int c0 = nt * cols_per_tile;
+
+    // weight row held by LDS tile row t
+    auto wrow = [&](int t) __attribute__((always_inline)) -> int {
+      int n;
+      if constexpr (GATED) {
+        const int half = t / WN, q = t % WN;
+        n = c0 + half * (WN / 2) + (q % (WN / 2));
+      } else {
+        n = c0 + t;
+      }
+      return min(n, p.N - 1);
+    };
+    auto is_up = [&](int t) __attribute__((always_inline)) -> bool { return GATED && (t % WN) >= WN / 2; };
+
+    // global -> LDS mapping in 16-byte chunks: chunk i of thread tid covers tile row
+    // (tid / CPR) + i * (256 / CPR) and column chunk tid % CPR (CPR = chunks per 64-wide row).
+    // Addresses are recomputed per load from a few base values instead of being held in
+    // registers. Activation rows past the expert's end are not loaded: their LDS rows (stale
+    // but finite data) only feed output rows that are never stored, and MFMA rows are
+    // independent.
+    constexpr int ACPR = 8, ARPI = NTH / ACPR;                       // A: chunks per row, rows per i
+    constexpr int BCPR = (WF == kFP8) ? 4 : 8, BRPI = NTH / BCPR;    // B
+    constexpr int BELEM = (WF == kFP8) ? 16 : 8;                     // elements per B chunk
+    const int a_r = tid / ACPR, a_c = tid % ACPR;
+    const int b_r = tid / BCPR, b_c = tid % BCPR;
+    const uint16_t* xa = static_cast<const uint16_t*>(p.X) + (size_t)r0 * p.K + a_c * 8;
+    const char* w1 = static_cast<const char*>(p.W1) + ((size_t)e * wstride + b_c * BELEM) * (WF == kFP8 ? 1 : 2);
+    const char* w2 = GATED ? static_cast<const char*>(p.W2) + ((size_t)e * wstride + b_c * BELEM) * (WF == kFP8 ? 1 : 2) : w1;
+
+    struct Stage {
+      u32x4 a[ACH];
+      u32x4 b[BCH];
+    };
+    auto gload = [&](int kb, Stage st) __attribute__((always_inline)) -> Stage {
+      const size_t ko = (size_t)kb * kTK;
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) {
+        const int row = a_r + i * ARPI;
+        if (row < nrows) st.a[i] = *reinterpret_cast<const u32x4*>(xa + (size_t)row * p.K + ko);
+      }
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        const int t = b_r + i * BRPI;
+        const char* base = is_up(t) ? w2 : w1;
+        st.b[i] = *reinterpret_cast<const u32x4*>(base + ((size_t)wrow(t) * p.K + ko) * (WF == kFP8 ? 1 : 2));
+      }
+      return st;
+    };
+    // (ARPI and BRPI are multiples of 16, so the swizzle term of row + i * RPI equals row's)
+    auto lstore = [&](int buf, const Stage& st) __attribute__((always_inline)) {
+      __bf16* A = lds_a + buf * TM * kLdsRow + swz(a_r, a_c);
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(A + i * ARPI * kLdsRow) = st.a[i];
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        if constexpr (WF == kFP8) {
+          __bf16* B = lds_b + buf * TN * kLdsRow + (b_r + i * BRPI) * kLdsRow;
+          *reinterpret_cast<bf16x8*>(B + ((((2 * b_c) ^ ((b_r >> 1) & 7))) << 3)) =
+              fp8x8_to_bf16(make_uint2(st.b[i][0], st.b[i][1]));
+          *reinterpret_cast<bf16x8*>(B + ((((2 * b_c + 1) ^ ((b_r >> 1) & 7))) << 3)) =
+              fp8x8_to_bf16(make_uint2(st.b[i][2], st.b[i][3]));
+        } else {
+          __bf16* B = lds_b + buf * TN * kLdsRow + swz(b_r, b_c);
+          *reinterpret_cast<u32x4*>(B + i * BRPI * kLdsRow) = st.b[i];
+        }
+      }
+    };
+
+    constexpr int PF = (WF == kFP8) ? MF : 1;   // fp8: per-block partial sums
+    f32x4 acc[MF][NF], part[PF][(WF == kFP8) ? NF : 1];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+#pragma unroll
+      for (int j = 0; j < ((WF == kFP8) ? NF : 1); ++j) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Stage stage{};
+    stage = gload(0, stage);
+    lstore(0, stage);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      if (kb + 1 < nkb) stage = gload(kb + 1, stage);
+      const __bf16* A = lds_a + buf * TM * kLdsRow;
+      const __bf16* B = lds_b + buf * TN * kLdsRow;
+#pragma unroll
+      for (int ks = 0; ks < kTK / 32; ++ks) {
+        // all fragment reads of this 32-long step first, then the MFMAs, so that the LDS
+        // latency of later fragments overlaps the MFMAs of earlier ones
+        const int chunk = ks * 4 + (lane >> 4);
+        bf16x8 bfr[NF], afr[MF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+          bfr[nf] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + nf * 16 + (lane & 15), chunk));
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+          afr[mf] = *reinterpret_cast<const bf16x8*>(A + swz(wm * WM + mf * 16 + (lane & 15), chunk));
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            if constexpr (WF == kFP8)
+              part[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], part[mf][nf], 0, 0, 0);
+            else
+              acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+          }
+      }
+      if constexpr (WF == kFP8) {
+        // end of a 128-long contraction block (two steps): scale the partial sums
+        if ((kb & 1) == 1 || kb + 1 == nkb) {
+          const int kb128 = (kb * kTK) / 128;
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            const int t = wn * WN + nf * 16;       // LDS tile row of this fragment
+            const float* S = is_up(t) ? p.S2 : p.S1;
+            const float sc = S[((size_t)e * nNB128 + wrow(t) / 128) * nKB128 + kb128];
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[mf][nf][j] = fmaf(sc, part[mf][nf][j], acc[mf][nf][j]);
+              part[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        }
+      }
+      if (kb + 1 < nkb) lstore(buf ^ 1, stage);
+      __syncthreads();
+    }
+
+    // epilogue from registers: lane holds rows (lane/16)*4 + j, column lane%16 of each fragment
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wm * WM + mf * 16 + (lane >> 4) * 4 + j;
+        if (r >= nrows) continue;
+        const size_t orow = (size_t)(r0 + r) * p.N;
+        if constexpr (GATED) {
+#pragma unroll
+          for (int nf = 0; nf < NF / 2; ++nf) {
+            const int col = c0 + wn * (WN / 2) + nf * 16 + (lane & 15);
+            if (col < p.N)
+              static_cast<__bf16*>(p.out)[orow + col] = (__bf16)(silu(acc[mf][nf][j]) * acc[mf][nf + NF / 2][j]);
+          }
+        } else {
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            const int col = c0 + wn * WN + nf * 16 + (lane & 15);
+            if (col < p.N) static_cast<float*>(p.out)[orow + col] = acc[mf][nf][j];
+          }
+        }
+      }
+  }
+}
+
+template <int WF, bool GATED, int WM, int WN, int WGM, int WGN>
+static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
+  constexpr int NTH = 64 * WGM * WGN;
+  const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + NTH) * sizeof(int32_t) +
+                     (size_t)2 * (WGM * WM + WGN * WN) * kLdsRow * sizeof(__bf16);
+  auto kern = &ffn_tiled_kernel<WF, GATED, WM, WN, WGM, WGN>;
+  if (lds > 64 * 1024) {
+    hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (st != hipSuccess) return st;
+  }
+  const int per_cu = lds > 80 * 1024 ? 1 : 2;
+  kern<<<dev.num_cus * per_cu, NTH, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Tiled kernel with direct-to-LDS operand loads (bf16 weights). Same tile decomposition as
+// ffn_tiled_kernel, but operands go from memory straight into LDS (global_load_lds, 16 bytes
+// per lane, no register staging) through a ring of kRing 32-wide contraction steps, keeping
+// kRing-1 steps of loads in flight while the MFMAs consume the oldest one: enough to cover
+// L2-miss latency at the MFMA rate of a 256 x 256 tile. LDS rows are 32 bf16 (64 bytes = 4
+// chunks of 16 bytes) with chunk c of row r stored at chunk c ^ ((r >> 2) & 3), which makes the
+// 16-row fragment loads conflict-free; the loading lanes pick their source addresses so that
+// the linear LDS image is the swizzled tile.
+constexpr int kDK = 32;     // contraction step
+constexpr int kRing = 4;    // LDS ring depth
+
+__device__ __forceinline__ int dswz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others are left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool GATED, int WM, int WN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
+  constexpr int NW = WGM * WGN, NTH = 64 * NW;
+  constexpr int TM = WGM * WM, TN = WGN * WN;
+  constexpr int MF = WM / 16, NF = WN / 16;
+  constexpr int AI = TM / 16, BI = TN / 16;             // 1 KB load instructions per step
+  static_assert(AI % NW == 0 && BI % NW == 0, "loads must split evenly over waves");
+  constexpr int AIW = AI / NW, BIW = BI / NW;           // per wave
+  constexpr int LPW = AIW + BIW;                        // loads per wave per step
+  constexpr int STAGE = (TM + TN) * 4;                  // 16-byte chunks per ring slot
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Epad = (p.E + 1 + 3) & ~3;
+  int32_t* pre = reinterpret_cast<int32_t*>(smem);
+  int32_t* offs = pre + Epad;
+  int32_t* scan_tmp = offs + Epad;
+  u32x4* ring = reinterpret_cast<u32x4*>(scan_tmp + ((NTH + 3) & ~3));   // [kRing][STAGE]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  constexpr int cols_per_tile = GATED ? TN / 2 : TN;
+  const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
+  build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, 0x7fffffff, NT, offs, p.min_rows, TM);
+  const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
+  const int nst = p.K / kDK;  // K is a multiple of 64 on this path
+  const size_t wstride = (size_t)p.N * p.K;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = p.E;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(pre[mid]) <= item) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int local = item - __builtin_amdgcn_readfirstlane(pre[e]);
+    constexpr int kGroupM = 4;
+    const int ebeg = __builtin_amdgcn_readfirstlane(offs[e]);
+    const int MT = (__builtin_amdgcn_readfirstlane(offs[e + 1]) - ebeg + TM - 1) / TM;
+    const int g = local / (kGroupM * NT);
+    const int gm = min(kGroupM, MT - g * kGroupM);
+    const int j = local - g * kGroupM * NT;
+    const int nt = j / gm;
+    const int mt = g * kGroupM + j % gm;
+    const int r0 = ebeg + mt * TM;
+    const int nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
+    const int c0 = nt * cols_per_tile;
+
+    // per-lane source of each of this wave's load instructions (element offsets at step 0)
+    size_t a_src[AIW], b_src[BIW];
+    bool b_up[BIW];
+#pragma unroll
+    for (int i = 0; i < AIW; ++i) {
+      const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the A tile
+      const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
+      a_src[i] = (size_t)(r0 + min(r, nrows - 1)) * p.K + c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < BIW; ++i) {
+      const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the B tile
+      const int t = q >> 2, c = (q & 3) ^ ((t >> 2) & 3);
+      int n;
+      if constexpr (GATED) {
+        const int blk = t / WN, qq = t % WN;
+        b_up[i] = qq >= WN / 2;
+        n = c0 + blk * (WN / 2) + (qq % (WN / 2));
+      } else {
+        b_up[i] = false;
+        n = c0 + t;
+      }
+      b_src[i] = (size_t)e * wstride + (size_t)min(n, p.N - 1) * p.K + c * 8;
+    }
+    const uint16_t* X = static_cast<const uint16_t*>(p.X);
+    const uint16_t* W1 = static_cast<const uint16_t*>(p.W1);
+    const uint16_t* W2 = GATED ? static_cast<const uint16_t*>(p.W2) : W1;
+
+    auto issue = [&](int st) __attribute__((always_inline)) {
+      u32x4* slot = ring + (st % kRing) * STAGE;
+      const size_t ko = (size_t)st * kDK;
+#pragma unroll
+      for (int i = 0; i < AIW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(X + a_src[i] + ko),
+            (__attribute__((address_space(3))) void*)(slot + (wave + i * NW) * 64), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BIW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)((b_up[i] ? W2 : W1) + b_src[i] + ko),
+            (__attribute__((address_space(3))) void*)(slot + TM * 4 + (wave + i * NW) * 64), 16, 0, 0);
+    };
+
+    f32x4 acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int jj = 0; jj < NF; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int st = 0; st < kRing - 1; ++st)
+      if (st < nst) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      // this wave's loads of step st are done once at most the later steps' loads are pending
+      const int later = min(kRing - 2, nst - 1 - st);
+      if (later >= 2) wait_vmcnt<2 * LPW>();
+      else if (later == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      // every wave's loads of step st have landed (the wait above) and every wave is done
+      // reading the slot of step st-1. A bare s_barrier: a fence here would make the compiler
+      // drain all outstanding direct-to-LDS loads. The signal fences only stop the compiler
+      // from moving LDS accesses across the barrier.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (st + kRing - 1 < nst) issue(st + kRing - 1);
+      const u32x4* slot = ring + (st % kRing) * STAGE;
+      const int c = lane >> 4;
+      bf16x8 bfr[NF], afr[MF];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const u32x4 v = slot[TM * 4 + dswz(wn * WN + nf * 16 + (lane & 15), c)];
+        __builtin_memcpy(&bfr[nf], &v, 16);
+      }
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        const u32x4 v = slot[dswz(wm * WM + mf * 16 + (lane & 15), c)];
+        __builtin_memcpy(&afr[mf], &v, 16);
+      }
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+    }
+    __syncthreads();  // all waves done reading the ring before the next item refills it
+
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) {
+        const int r = wm * WM + mf * 16 + (lane >> 4) * 4 + jr;
+        if (r >= nrows) continue;
+        const size_t orow = (size_t)(r0 + r) * p.N;
+        if constexpr (GATED) {
+#pragma unroll
+          for (int nf = 0; nf < NF / 2; ++nf) {
+            const int col = c0 + wn * (WN / 2) + nf * 16 + (lane & 15);
+            if (col < p.N)
+              static_cast<__bf16*>(p.out)[orow + col] = (__bf16)(silu(acc[mf][nf][jr]) * acc[mf][nf + NF / 2][jr]);
+          }
+        } else {
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            const int col = c0 + wn * WN + nf * 16 + (lane & 15);
+            if (col < p.N) static_cast<float*>(p.out)[orow + col] = acc[mf][nf][jr];
+          }
+        }
+      }
+  }
+}
+
+template <bool GATED, int WM, int WN, int WGM, int WGN>
+static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
+  constexpr int NTH = 64 * WGM * WGN;
+  const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + ((NTH + 3) & ~3)) * sizeof(int32_t) +
+                     (size_t)kRing * (WGM * WM + WGN * WN) * 4 * 16;
+  auto kern = &ffn_tiled_dl_kernel<GATED, WM, WN, WGM, WGN>;
+  if (lds > 64 * 1024) {
+    hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (st != hipSuccess) return st;
+  }
+  const int per_cu = lds > 80 * 1024 ? 1 : 2;
+  kern<<<dev.num_cus * per_cu, NTH, lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -370,24 +888,42 @@ size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, mo
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
+  // bf16 activations with 64-multiple widths: experts with more than kStreamMaxRows rows go
+  // to the tiled kernel, the rest are streamed; otherwise (fp32, odd widths) all stream
+  const bool tiled = a.act == MOE_BF16 && a.d % kTK == 0 && a.d_ff % kTK == 0;
+  const int small = tiled ? kStreamMaxRows : 0x7fffffff;
   StreamArgs gu{a.x_sorted, a.w_gate, a.w_up, a.s_gate, a.s_up, a.h, a.offsets,
-                a.E, a.d, a.d_ff, a.rows, 0x7fffffff};
+                a.E, a.d, a.d_ff, a.rows, small};
   StreamArgs dn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
-                a.E, a.d_ff, a.d, a.rows, 0x7fffffff};
+                a.E, a.d_ff, a.d, a.rows, small};
+  TiledArgs tgu{a.x_sorted, a.w_gate, a.w_up, a.s_gate, a.s_up, a.h, a.offsets,
+                a.E, a.d, a.d_ff, a.rows, small};
+  TiledArgs tdn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
+                a.E, a.d_ff, a.d, a.rows, small};
   hipError_t st;
   if (a.act == MOE_F32) {
-    st = launch_stream<kF32, kF32, 2, 1, 2>(gu, dev, stream);
+    st = launch_stream<kF32, kF32, 2, 1, 1, 4>(gu, dev, stream);
     if (st != hipSuccess) return st;
-    return launch_stream<kF32, kF32, 1, 2, 2>(dn, dev, stream);
+    return launch_stream<kF32, kF32, 1, 2, 1, 4>(dn, dev, stream);
   }
+  // prefill-sized batches (at least 32 rows per expert on average) take the large tile
+  const bool big = (long long)a.rows >= 32LL * a.E;
   if (a.wdt == MOE_BF16) {
-    st = launch_stream<kBF16, kBF16, 2, 2, 4>(gu, dev, stream);
-    if (st != hipSuccess) return st;
-    return launch_stream<kBF16, kBF16, 1, 4, 4>(dn, dev, stream);
+    st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
+    if (st == hipSuccess && tiled)
+      st = big ? launch_tiled_dl<true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled<kBF16, true, 64, 64, 2, 2>(tgu, dev, stream);
+    if (st == hipSuccess) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
+    if (st == hipSuccess && tiled)
+      st = big ? launch_tiled_dl<false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled<kBF16, false, 64, 64, 2, 2>(tdn, dev, stream);
+    return st;
   }
-  st = launch_stream<kBF16, kFP8, 2, 2, 4>(gu, dev, stream);
-  if (st != hipSuccess) return st;
-  return launch_stream<kBF16, kFP8, 1, 4, 4>(dn, dev, stream);
+  st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
+  if (st == hipSuccess && tiled)
+    st = big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream) : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
+  if (st == hipSuccess) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
+  if (st == hipSuccess && tiled)
+    st = big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream) : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
+  return st;
 }
 
 }  // namespace moe

@@ -156,6 +156,17 @@ def test_dims_not_multiples_of_tiles(dev, act, w, d, d_ff):
     run_full(synth.tiny_config(T=70, d=d, E=6, k=3, d_ff=d_ff, act=act, w=w, zipf_s=1.0, seed=7), dev)
 
 
+@pytest.mark.parametrize("w,E,zipf", [("bf16", 5, 1.0), ("bf16", 40, 1.5), ("fp8_e4m3fn", 40, 1.5)])
+def test_prefill_tile_paths(dev, w, E, zipf):
+    # T*k >= 32*E selects the prefill tiles (256-row tiles; direct-to-LDS ring for bf16);
+    # skewed counts also leave some experts with <= 16 rows on the streaming kernel, and no
+    # expert's row count is a multiple of the tile
+    d, d_ff = (192, 320) if w == "bf16" else (256, 384)
+    cfg = synth.tiny_config(T=700, d=d, E=E, k=2, d_ff=d_ff, act="bf16", w=w, zipf_s=zipf, seed=13)
+    got, _ = run_full(cfg, dev)
+    assert cfg.T * cfg.k >= 32 * cfg.E
+
+
 def test_fp8_small(dev):
     run_full(synth.tiny_config(T=90, d=256, E=6, k=2, d_ff=384, act="bf16", w="fp8_e4m3fn",
                                zipf_s=1.0, seed=8), dev)

@@ -178,8 +178,10 @@ def test_many_experts_and_topk_limits(dev):
     run_full(synth.tiny_config(T=20, d=128, E=1024, k=32, d_ff=256, act="bf16", w="bf16", seed=9), dev)
 
 
-def test_ties_and_signed_zero(dev):
-    cfg = synth.tiny_config(T=64, d=64, E=12, k=3, d_ff=64, act="f32", w="f32", seed=10)
+@pytest.mark.parametrize("E,k", [(12, 3), (300, 7)])
+def test_ties_and_signed_zero(dev, E, k):
+    # integer-valued logits: many exact ties, within a lane's experts and across wave rows
+    cfg = synth.tiny_config(T=64, d=64, E=E, k=k, d_ff=64, act="f32", w="f32", seed=10)
     rng = np.random.default_rng(10)
     lg = rng.integers(-1, 2, size=(cfg.T, cfg.E)).astype(np.float32)
     lg[lg == 0] = np.where(rng.random(np.count_nonzero(lg == 0)) < 0.5, -0.0, 0.0).astype(np.float32)

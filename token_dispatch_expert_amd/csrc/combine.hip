@@ -1,48 +1,65 @@
-// Un-permute and gate-weighted combine, one workgroup per token.
+// Un-permute and gate-weighted combine.
 //
 // Operation: "Expert Parallelism" tutorial page, section 4, combine: results go back to the
 // original token order and each token's k expert outputs are summed with their gate
 // weights. Reading taken: fp32 sum in slot order j = 0..k-1 (no atomics, deterministic).
 //
-// HBM-bound: each token reads its k fp32 rows of y_sorted (16-byte vectors, coalesced across
-// the workgroup) and writes one fp32 row. The row indices and gates are uniform per
-// workgroup, so they come through scalar loads.
+// HBM-bound: each token reads its k fp32 rows of y_sorted and writes one fp32 row. A
+// workgroup covers one token and a 256-vector (4 KB) slice of its row, so even a small batch
+// launches enough workgroups; each thread first issues the loads of up to 8 slots (independent
+// 16-byte loads in flight together), then accumulates them in slot order. Row indices and
+// gates are uniform per workgroup and come through scalar loads.
 #include "moe_internal.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ ys,
-                                                      const int32_t* __restrict__ f2s,
-                                                      const float* __restrict__ gates, int k,
-                                                      int vec_per_row, int R,
-                                                      float4* __restrict__ y) {
-  const int t = blockIdx.x;
+constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 8;  // slots whose loads are in flight together
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float4* __restrict__ ys,
+                                                                  const int32_t* __restrict__ f2s,
+                                                                  const float* __restrict__ gates,
+                                                                  int k, int vec_per_row, int R,
+                                                                  int slices,
+                                                                  float4* __restrict__ y) {
+  const int t = blockIdx.x / slices;
+  const int v = (blockIdx.x % slices) * kCombineThreads + threadIdx.x;
+  if (v >= vec_per_row) return;
   const int32_t* pos = f2s + (size_t)t * k;
   const float* g = gates + (size_t)t * k;
-  for (int v = threadIdx.x; v < vec_per_row; v += blockDim.x) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[j];
-      if ((unsigned)p >= (unsigned)R) continue;  // corrupt map: never read out of bounds
-      const float w = g[j];
-      const float4 r = ys[(size_t)p * vec_per_row + v];
-      acc.x = fmaf(w, r.x, acc.x);
-      acc.y = fmaf(w, r.y, acc.y);
-      acc.z = fmaf(w, r.z, acc.z);
-      acc.w = fmaf(w, r.w, acc.w);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    float4 r[kCombineBatch];
+    float w[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int j = j0 + u;
+      const int p = j < k ? pos[j] : -1;
+      const bool ok = (unsigned)p < (unsigned)R;  // a corrupt map never reads out of bounds
+      w[u] = ok ? g[j] : 0.f;
+      r[u] = ok ? ys[(size_t)p * vec_per_row + v] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    y[(size_t)t * vec_per_row + v] = acc;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (j0 + u < k) {
+        acc.x = fmaf(w[u], r[u].x, acc.x);
+        acc.y = fmaf(w[u], r[u].y, acc.y);
+        acc.z = fmaf(w[u], r[u].z, acc.z);
+        acc.w = fmaf(w[u], r[u].w, acc.w);
+      }
+    }
   }
+  y[(size_t)t * vec_per_row + v] = acc;
 }
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* flat_to_sorted,
                           const float* gates, int T, int k, int d, float* y, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int vpr = d / 4;
-  const int threads = vpr >= 256 ? 256 : ((vpr + kWave - 1) / kWave) * kWave;
-  combine_kernel<<<T, threads, 0, stream>>>(reinterpret_cast<const float4*>(y_sorted),
-                                            flat_to_sorted, gates, k, vpr, T * k,
-                                            reinterpret_cast<float4*>(y));
+  const int slices = (vpr + kCombineThreads - 1) / kCombineThreads;
+  combine_kernel<<<(unsigned)T * slices, kCombineThreads, 0, stream>>>(
+      reinterpret_cast<const float4*>(y_sorted), flat_to_sorted, gates, k, vpr, T * k, slices,
+      reinterpret_cast<float4*>(y));
   return hipGetLastError();
 }
 

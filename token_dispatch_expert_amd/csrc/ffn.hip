@@ -27,6 +27,8 @@
 // added to the running sum times the block's scale.
 #include <math.h>
 
+#include <utility>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -703,6 +705,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// the same with a wave-uniform runtime count in [0, MAX] (a scalar branch per candidate)
+template <int... Ns>
+__device__ __forceinline__ void wait_vmcnt_dyn_impl(int n, std::integer_sequence<int, Ns...>) {
+  ((n == Ns ? (wait_vmcnt<Ns>(), 0) : 0), ...);
+}
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  wait_vmcnt_dyn_impl(n, std::make_integer_sequence<int, MAX + 1>{});
+}
 
 template <bool GATED, int WM, int WN, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
@@ -751,6 +762,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
     const int r0 = ebeg + mt * TM;
     const int nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
     const int c0 = nt * cols_per_tile;
+    // A load instructions cover 16 tile rows each; those wholly past the expert's last row are
+    // skipped (their LDS rows only feed output rows that are never stored). This wave's load
+    // count per step is then aiw + BIW, uniform over the item.
+    int aiw = 0;
+#pragma unroll
+    for (int i = 0; i < AIW; ++i) aiw += 1;
+    const int lpw = aiw + BIW;
 
     // per-lane source of each of this wave's load instructions (element offsets at step 0)
     size_t a_src[AIW], b_src[BIW];
@@ -785,9 +803,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       const size_t ko = (size_t)st * kDK;
 #pragma unroll
       for (int i = 0; i < AIW; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(X + a_src[i] + ko),
-            (__attribute__((address_space(3))) void*)(slot + (wave + i * NW) * 64), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(X + a_src[i] + ko),
+              (__attribute__((address_space(3))) void*)(slot + (wave + i * NW) * 64), 16, 0, 0);
 #pragma unroll
       for (int i = 0; i < BIW; ++i)
         __builtin_amdgcn_global_load_lds(
@@ -807,9 +825,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of step st are done once at most the later steps' loads are pending
       const int later = min(kRing - 2, nst - 1 - st);
-      if (later >= 2) wait_vmcnt<2 * LPW>();
-      else if (later == 1) wait_vmcnt<LPW>();
-      else wait_vmcnt<0>();
+      wait_vmcnt_dyn<(kRing - 2) * LPW>(later * lpw);
       // every wave's loads of step st have landed (the wait above) and every wave is done
       // reading the slot of step st-1. A bare s_barrier: a fence here would make the compiler
       // drain all outstanding direct-to-LDS loads. The signal fences only stop the compiler
@@ -888,10 +904,16 @@ size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, mo
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  // bf16 activations with 64-multiple widths: experts with more than kStreamMaxRows rows go
-  // to the tiled kernel, the rest are streamed; otherwise (fp32, odd widths) all stream
+  // Which kernel takes which expert (decided per expert on the device from its row count):
+  //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
+  //  - bf16/fp8 decode-sized batches (T*k < 32*E): bf16 weights go to the 128-row
+  //    direct-to-LDS tiles for every expert; fp8 weights stream experts with <= 16 rows and
+  //    tile the rest;
+  //  - prefill-sized batches: experts with <= 16 rows stream, the rest take 256-row tiles.
   const bool tiled = a.act == MOE_BF16 && a.d % kTK == 0 && a.d_ff % kTK == 0;
-  const int small = tiled ? kStreamMaxRows : 0x7fffffff;
+  const bool big = (long long)a.rows >= 32LL * a.E;
+  int small = tiled ? kStreamMaxRows : 0x7fffffff;
+  if (tiled && !big && a.wdt == MOE_BF16) small = 0;
   StreamArgs gu{a.x_sorted, a.w_gate, a.w_up, a.s_gate, a.s_up, a.h, a.offsets,
                 a.E, a.d, a.d_ff, a.rows, small};
   StreamArgs dn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
@@ -900,21 +922,20 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
                 a.E, a.d, a.d_ff, a.rows, small};
   TiledArgs tdn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
                 a.E, a.d_ff, a.d, a.rows, small};
-  hipError_t st;
+  const bool stream_pass = small > 0;
+  hipError_t st = hipSuccess;
   if (a.act == MOE_F32) {
     st = launch_stream<kF32, kF32, 2, 1, 1, 4>(gu, dev, stream);
-    if (st != hipSuccess) return st;
-    return launch_stream<kF32, kF32, 1, 2, 1, 4>(dn, dev, stream);
+    if (st == hipSuccess) st = launch_stream<kF32, kF32, 1, 2, 1, 4>(dn, dev, stream);
+    return st;
   }
-  // prefill-sized batches (at least 32 rows per expert on average) take the large tile
-  const bool big = (long long)a.rows >= 32LL * a.E;
   if (a.wdt == MOE_BF16) {
-    st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
+    if (stream_pass) st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled<kBF16, true, 64, 64, 2, 2>(tgu, dev, stream);
-    if (st == hipSuccess) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
+      st = big ? launch_tiled_dl<true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled_dl<true, 64, 64, 2, 2>(tgu, dev, stream);
+    if (st == hipSuccess && stream_pass) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled<kBF16, false, 64, 64, 2, 2>(tdn, dev, stream);
+      st = big ? launch_tiled_dl<false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled_dl<false, 64, 64, 2, 2>(tdn, dev, stream);
     return st;
   }
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);

@@ -6,7 +6,9 @@
 // the flat index i = t*k + j, so within an expert rows appear in token order and the
 // permutation is unique (the k experts of one token are distinct).
 //
-// Four launches, none using float atomics, all deterministic:
+// Batches of more than kSmallR assignments take four launches, none using float atomics, all
+// deterministic (smaller batches use one workgroup for the first three, see
+// permute_small_kernel):
 //   hist : one workgroup per tile of kPermuteTile flat entries; LDS histogram -> ws[tile][e]
 //   scan : one workgroup; per expert an exclusive prefix over tiles, then counts, the
 //          exclusive scan over experts (offsets) and per-tile bases ws[tile][e]
@@ -131,6 +133,85 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   }
 }
 
+// Small batches (R <= kSmallR): one workgroup of 16 waves does histogram, scan and stable
+// rank. The R entries are split into 16 contiguous slices, one per wave (slice order = flat
+// order). Each wave ranks its slice 64 entries at a time with the ballot match (ids staged in
+// LDS first) and keeps a per-expert running count in its own LDS row; a prefix over the 16
+// rows plus the exclusive scan over experts then gives every slice's base per expert.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallChunks = 8;  // 64-entry chunks per wave -> R <= 16 * 8 * 64
+constexpr int kSmallR = kSmallWaves * kSmallChunks * kWave;
+
+__global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ s2f, int32_t* __restrict__ f2s) {
+  extern __shared__ int32_t sm[];
+  int32_t* wc = sm;                                  // [16][E] per-wave counts, then bases
+  int32_t* sc = wc + kSmallWaves * E;                // [1024] scan
+  int32_t* key = sc + kSmallWaves * kWave;           // [R] staged (clamped) expert ids
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  for (int i = tid; i < kSmallWaves * E; i += blockDim.x) wc[i] = 0;
+  for (int i = tid; i < R; i += blockDim.x) key[i] = clamp_expert(ids[i], E);
+  __syncthreads();
+
+  const int slice = ((R + kSmallWaves - 1) / kSmallWaves + kWave - 1) / kWave * kWave;
+  const int lo = min(wave * slice, R), hi = min(lo + slice, R);
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int32_t* mine = wc + wave * E;
+  int rank[kSmallChunks], exp_[kSmallChunks];
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int i = lo + c * kWave + lane;
+    const bool valid = i < hi;
+    const int e = valid ? key[i] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    exp_[c] = e;
+    rank[c] = valid ? mine[e] + __popcll(same & lower) : 0;
+    // LDS ops of one wave complete in order: every lane's read above precedes this update
+    if (valid && (63 - __clzll(same)) == lane) mine[e] += __popcll(same);
+  }
+  __syncthreads();
+
+  int total = 0;
+  if (tid < E) {
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int t = wc[w * E + tid];
+      wc[w * E + tid] = total;
+      total += t;
+    }
+    counts[tid] = total;
+  }
+  sc[tid] = total;
+  __syncthreads();
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+    const int v = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int base = sc[tid] - total;
+    offsets[tid] = base;
+    for (int w = 0; w < kSmallWaves; ++w) wc[w * E + tid] += base;
+  }
+  if (tid == 0) offsets[E] = R;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int i = lo + c * kWave + lane;
+    if (i < hi) {
+      const int pos = mine[exp_[c]] + rank[c];
+      s2f[pos] = i;
+      f2s[i] = pos;
+    }
+  }
+}
+
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int T, int E, int k,
                           int d, int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat,
                           int32_t* flat_to_sorted, void* x_sorted, int32_t* ws,
@@ -138,6 +219,25 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
   const int R = T * k;
   const int n_tiles = (R + kPermuteTile - 1) / kPermuteTile;
   const size_t lds = (size_t)E * sizeof(int32_t);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int vpr = d * elem_bytes / 16;
+  const int threads = vpr >= 256 ? 256 : ((vpr + kWave - 1) / kWave) * kWave;
+  if (R > 0 && R <= kSmallR) {
+    const size_t slds = ((size_t)kSmallWaves * E + kSmallWaves * kWave + R) * sizeof(int32_t);
+    if (slds > 64 * 1024) {
+      hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(&permute_small_kernel),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
+      if (st != hipSuccess) return st;
+    }
+    permute_small_kernel<<<1, kSmallWaves * kWave, slds, stream>>>(ids, R, E, nbits, counts, offsets,
+                                                                   sorted_to_flat, flat_to_sorted);
+    hipError_t st = hipGetLastError();
+    if (st != hipSuccess) return st;
+    permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,
+                                                   flat_to_sorted, static_cast<uint4*>(x_sorted));
+    return hipGetLastError();
+  }
   if (n_tiles > 0) {
     permute_hist_kernel<<<n_tiles, 256, lds, stream>>>(ids, R, E, ws);
     hipError_t st = hipGetLastError();
@@ -146,14 +246,10 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
   permute_scan_kernel<<<1, kScanThreads, 0, stream>>>(ws, n_tiles, E, R, counts, offsets);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess || n_tiles == 0) return st;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
   permute_rank_kernel<<<n_tiles, kWave, lds, stream>>>(ids, R, E, nbits, ws, sorted_to_flat,
                                                         flat_to_sorted);
   st = hipGetLastError();
   if (st != hipSuccess) return st;
-  const int vpr = d * elem_bytes / 16;
-  const int threads = vpr >= 256 ? 256 : ((vpr + kWave - 1) / kWave) * kWave;
   permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,
                                                  flat_to_sorted, static_cast<uint4*>(x_sorted));
   return hipGetLastError();

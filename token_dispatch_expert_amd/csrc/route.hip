@@ -8,8 +8,10 @@
 //
 // Layout: lane L of the wave holds experts L, L+64, L+128, ... (coalesced row load). Each of
 // the k rounds takes every lane's best unchosen candidate and reduces it across the wave
-// with a butterfly under the total order (value desc, index asc), so every lane agrees on
-// the winner without a barrier. Slot j's result stays in lane j.
+// under the total order (value desc, index asc): DPP moves combine lanes inside each 16-lane
+// row (xor 1, xor 2, half-row mirror, row mirror), then the four row winners are read with
+// readlane and compared in scalar registers, so every lane agrees on the winner without LDS
+// traffic or a barrier. Slot j's result stays in lane j.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -28,6 +30,26 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t value, hipStream_t stream)
 }
 
 constexpr int kNone = 0x7fffffff;
+
+// (value, index) candidate order: a valid candidate beats none; larger value wins; equal values
+// go to the lower index.
+__device__ __forceinline__ bool better(float ov, int oi, float bv, int bi) {
+  return oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// DPP controls: quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror,
+// row_mirror.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
 // EPL = experts per lane (ceil(E / 64)).
 template <int EPL>
@@ -63,16 +85,24 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         bi = e;
       }
     }
+    dpp_step<kDppXor1>(bv, bi);
+    dpp_step<kDppXor2>(bv, bi);
+    dpp_step<kDppHalfMirror>(bv, bi);
+    dpp_step<kDppMirror>(bv, bi);
+    // row winners sit in every lane of their row; combine rows 0..3 in scalar registers
+    float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int wi = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      const bool take = oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi));
-      if (take) {
-        bv = ov;
-        bi = oi;
+    for (int r = 1; r < 4; ++r) {
+      const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+      const int ri = __builtin_amdgcn_readlane(bi, 16 * r);
+      if (better(rv, ri, wv, wi)) {
+        wv = rv;
+        wi = ri;
       }
     }
+    bv = wv;
+    bi = wi;
     if (lane == (bi & (kWave - 1))) taken |= 1u << (bi / kWave);
     if (lane == j) {
       slot_val = bv;

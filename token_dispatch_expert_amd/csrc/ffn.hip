@@ -129,6 +129,24 @@ __device__ __forceinline__ void expert_rows(const int32_t* offsets, int e, int r
 
 // Build the item prefix over experts in LDS: pre[e] = first item of expert e; pre[E] = total.
 // offs (optional) receives the clamped row offsets of every expert, offs[0..E].
+// Item of this workgroup in the round of a persistent grid that starts at item `base`, or -1.
+// The hardware deals workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), and
+// each XCD has its own L2. To let the workgroups of one XCD share operands, a round's n items
+// are cut into 8 runs of ceil(n / 8) consecutive items and run x goes to the workgroups of XCD
+// x; a short last round is thus spread over all XCDs. Grids that are not a multiple of 8 take
+// items in plain order.
+__device__ __forceinline__ int xcd_round_item(int base, int total) {
+  constexpr int kXcd = 8;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  if (G % kXcd != 0) return base + b < total ? base + b : -1;
+  const int n = min(G, total - base);
+  const int run = (n + kXcd - 1) / kXcd;
+  const int i = b / kXcd;
+  const int local = (b % kXcd) * run + i;
+  return (i < run && local < n) ? base + local : -1;
+}
+
 __device__ void build_item_prefix(int32_t* pre, int32_t* scratch, const int32_t* offsets, int E,
                                   int rows, int max_rows, int items_per_group,
                                   int32_t* offs = nullptr, int min_rows = 0,
@@ -487,7 +505,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_kernel(TiledArgs p) 
   const size_t wstride = (size_t)p.N * p.K;
   const int kl = (lane >> 4) * 8;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  for (int base = 0; base < total; base += gridDim.x) {
+    const int item = xcd_round_item(base, total);
+    if (item < 0) continue;  // uniform per workgroup
     int lo = 0, hi = p.E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -496,9 +516,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_kernel(TiledArgs p) 
     const int e = lo;
     const int local = item - __builtin_amdgcn_readfirstlane(pre[e]);
     // Tile order within an expert: groups of kGroupM row tiles, column tiles outer and row
-    // tiles inner within a group. Workgroups are dealt to the 8 XCDs round-robin, so the 32
-    // concurrent workgroups of one XCD cover 4 row tiles x 8 column tiles of the same expert
-    // and share both operands in that XCD's L2.
+    // tiles inner within a group. Consecutive items run on one XCD, so its concurrent
+    // workgroups cover kGroupM row tiles x several column tiles of the same expert and share
+    // both operands in that XCD's L2.
     constexpr int kGroupM = 4;
     const int ebeg = __builtin_amdgcn_readfirstlane(offs[e]);
     const int MT = (__builtin_amdgcn_readfirstlane(offs[e + 1]) - ebeg + TM - 1) / TM;
@@ -687,16 +707,26 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 // ---------------------------------------------------------------------------------------
 // Tiled kernel with direct-to-LDS operand loads (bf16 weights). Same tile decomposition as
 // ffn_tiled_kernel, but operands go from memory straight into LDS (global_load_lds, 16 bytes
-// per lane, no register staging) through a ring of kRing 32-wide contraction steps, keeping
-// kRing-1 steps of loads in flight while the MFMAs consume the oldest one: enough to cover
-// L2-miss latency at the MFMA rate of a 256 x 256 tile. LDS rows are 32 bf16 (64 bytes = 4
-// chunks of 16 bytes) with chunk c of row r stored at chunk c ^ ((r >> 2) & 3), which makes the
-// 16-row fragment loads conflict-free; the loading lanes pick their source addresses so that
-// the linear LDS image is the swizzled tile.
+// per lane, no register staging) through a ring of RING contraction steps of DK elements,
+// keeping RING-1 steps of loads in flight while the MFMAs consume the oldest one. Two shapes:
+//  - prefill, 256 x 256 tiles, DK = 32, 4 slots: the operands mostly hit in L2 and the ring
+//    covers L2-miss latency at the MFMA rate;
+//  - decode, 64 x 128 tiles, DK = 64, 3 slots, two workgroups per CU: weight streaming, where
+//    each weight row is read a full 128-byte line per step (64-byte pieces of many rows
+//    measured ~15% below line-sized ones in HBM throughput).
+// The loading lanes pick their source addresses so that the linear LDS image is the swizzled
+// tile (see dswz).
 constexpr int kDK = 32;     // contraction step
 constexpr int kRing = 4;    // LDS ring depth
 
-__device__ __forceinline__ int dswz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+// LDS image of a tile row of DK contraction elements (DK / 8 chunks of 16 bytes): chunk c of row
+// r sits at chunk c ^ x(r), x(r) = (r >> 2) & 3 for 4 chunks and (r >> 1) & 7 for 8 chunks, so
+// the 16 rows read by one fragment load (same chunk) fall on distinct banks.
+template <int DK>
+__device__ __forceinline__ int dswz(int row, int chunk) {
+  if constexpr (DK == 32) return row * 4 + (chunk ^ ((row >> 2) & 3));
+  else return row * 8 + (chunk ^ ((row >> 1) & 7));
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others are left at their maxima).
@@ -715,35 +745,42 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   wait_vmcnt_dyn_impl(n, std::make_integer_sequence<int, MAX + 1>{});
 }
 
-template <bool GATED, int WM, int WN, int WGM, int WGN>
+template <bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
+          bool ASKIP = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
+  static_assert(DK == 32 || DK == 64, "contraction step");
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
   constexpr int TM = WGM * WM, TN = WGN * WN;
   constexpr int MF = WM / 16, NF = WN / 16;
-  constexpr int AI = TM / 16, BI = TN / 16;             // 1 KB load instructions per step
-  static_assert(AI % NW == 0 && BI % NW == 0, "loads must split evenly over waves");
-  constexpr int AIW = AI / NW, BIW = BI / NW;           // per wave
-  constexpr int LPW = AIW + BIW;                        // loads per wave per step
-  constexpr int STAGE = (TM + TN) * 4;                  // 16-byte chunks per ring slot
+  constexpr int CPR = DK / 8;                           // 16-byte chunks per tile row
+  constexpr int AI = TM * CPR / 64, BI = TN * CPR / 64; // 1 KB load instructions per step
+  static_assert(BI % NW == 0 && (AI % NW == 0 || AI < NW), "loads must split evenly over waves");
+  // A loads per wave: AI / NW each, or (short tiles) one each for the first AI waves
+  constexpr int AIW = AI >= NW ? AI / NW : 1, BIW = BI / NW;
+  constexpr int LPW = AIW + BIW;                        // most loads per wave per step
+  constexpr int STAGE = (TM + TN) * CPR;                // 16-byte chunks per ring slot
   extern __shared__ __align__(16) unsigned char smem[];
   const int Epad = (p.E + 1 + 3) & ~3;
   int32_t* pre = reinterpret_cast<int32_t*>(smem);
   int32_t* offs = pre + Epad;
   int32_t* scan_tmp = offs + Epad;
-  u32x4* ring = reinterpret_cast<u32x4*>(scan_tmp + ((NTH + 3) & ~3));   // [kRing][STAGE]
+  u32x4* ring = reinterpret_cast<u32x4*>(scan_tmp + ((NTH + 3) & ~3));   // [RING][STAGE]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool loads_a = AI >= NW || wave < AI;  // wave-uniform
   const int wm = wave % WGM, wn = wave / WGM;
   constexpr int cols_per_tile = GATED ? TN / 2 : TN;
   const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
   build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, 0x7fffffff, NT, offs, p.min_rows, TM);
   const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
-  const int nst = p.K / kDK;  // K is a multiple of 64 on this path
+  const int nst = p.K / DK;  // K is a multiple of 64 on this path
   const size_t wstride = (size_t)p.N * p.K;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  for (int base = 0; base < total; base += gridDim.x) {
+    const int item = xcd_round_item(base, total);
+    if (item < 0) continue;  // uniform per workgroup
     int lo = 0, hi = p.E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -762,13 +799,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
     const int r0 = ebeg + mt * TM;
     const int nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
     const int c0 = nt * cols_per_tile;
-    // A load instructions cover 16 tile rows each; those wholly past the expert's last row are
-    // skipped (their LDS rows only feed output rows that are never stored). This wave's load
-    // count per step is then aiw + BIW, uniform over the item.
+    // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
+    // issued: those LDS rows keep stale data, which only reaches accumulator rows that are
+    // never stored (row r of the product depends on row r of A alone).
+    constexpr int RPI = 64 / CPR;  // tile rows per load instruction
     int aiw = 0;
 #pragma unroll
-    for (int i = 0; i < AIW; ++i) aiw += 1;
-    const int lpw = aiw + BIW;
+    for (int i = 0; i < AIW; ++i)
+      aiw += (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows)) ? 1 : 0;
+    const int lpw = aiw + BIW;  // this wave's loads per step
 
     // per-lane source of each of this wave's load instructions (element offsets at step 0)
     size_t a_src[AIW], b_src[BIW];
@@ -776,13 +815,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
 #pragma unroll
     for (int i = 0; i < AIW; ++i) {
       const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the A tile
-      const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
+      const int r = q / CPR, c = dswz<DK>(r, q % CPR) - r * CPR;  // source chunk (XOR involution)
       a_src[i] = (size_t)(r0 + min(r, nrows - 1)) * p.K + c * 8;
     }
 #pragma unroll
     for (int i = 0; i < BIW; ++i) {
       const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the B tile
-      const int t = q >> 2, c = (q & 3) ^ ((t >> 2) & 3);
+      const int t = q / CPR, c = dswz<DK>(t, q % CPR) - t * CPR;
       int n;
       if constexpr (GATED) {
         const int blk = t / WN, qq = t % WN;
@@ -799,10 +838,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
     const uint16_t* W2 = GATED ? static_cast<const uint16_t*>(p.W2) : W1;
 
     auto issue = [&](int st) __attribute__((always_inline)) {
-      u32x4* slot = ring + (st % kRing) * STAGE;
-      const size_t ko = (size_t)st * kDK;
+      u32x4* slot = ring + (st % RING) * STAGE;
+      const size_t ko = (size_t)st * DK;
 #pragma unroll
       for (int i = 0; i < AIW; ++i)
+        if (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows))
           __builtin_amdgcn_global_load_lds(
               (const __attribute__((address_space(1))) void*)(X + a_src[i] + ko),
               (__attribute__((address_space(3))) void*)(slot + (wave + i * NW) * 64), 16, 0, 0);
@@ -810,7 +850,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       for (int i = 0; i < BIW; ++i)
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)((b_up[i] ? W2 : W1) + b_src[i] + ko),
-            (__attribute__((address_space(3))) void*)(slot + TM * 4 + (wave + i * NW) * 64), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(slot + TM * CPR + (wave + i * NW) * 64), 16, 0, 0);
     };
 
     f32x4 acc[MF][NF];
@@ -820,12 +860,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       for (int jj = 0; jj < NF; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int st = 0; st < kRing - 1; ++st)
+    for (int st = 0; st < RING - 1; ++st)
       if (st < nst) issue(st);
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of step st are done once at most the later steps' loads are pending
-      const int later = min(kRing - 2, nst - 1 - st);
-      wait_vmcnt_dyn<(kRing - 2) * LPW>(later * lpw);
+      const int later = min(RING - 2, nst - 1 - st);
+      wait_vmcnt_dyn<(RING - 2) * LPW>(later * lpw);
       // every wave's loads of step st have landed (the wait above) and every wave is done
       // reading the slot of step st-1. A bare s_barrier: a fence here would make the compiler
       // drain all outstanding direct-to-LDS loads. The signal fences only stop the compiler
@@ -833,25 +873,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (st + kRing - 1 < nst) issue(st + kRing - 1);
-      const u32x4* slot = ring + (st % kRing) * STAGE;
-      const int c = lane >> 4;
-      bf16x8 bfr[NF], afr[MF];
+      if (st + RING - 1 < nst) issue(st + RING - 1);
+      const u32x4* slot = ring + (st % RING) * STAGE;
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf) {
-        const u32x4 v = slot[TM * 4 + dswz(wn * WN + nf * 16 + (lane & 15), c)];
-        __builtin_memcpy(&bfr[nf], &v, 16);
+      for (int h = 0; h < DK / 32; ++h) {  // 32-wide MFMA contraction slices of the step
+        const int c = h * 4 + (lane >> 4);
+        bf16x8 bfr[NF], afr[MF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+          const u32x4 v = slot[TM * CPR + dswz<DK>(wn * WN + nf * 16 + (lane & 15), c)];
+          __builtin_memcpy(&bfr[nf], &v, 16);
+        }
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+          const u32x4 v = slot[dswz<DK>(wm * WM + mf * 16 + (lane & 15), c)];
+          __builtin_memcpy(&afr[mf], &v, 16);
+        }
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
       }
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        const u32x4 v = slot[dswz(wm * WM + mf * 16 + (lane & 15), c)];
-        __builtin_memcpy(&afr[mf], &v, 16);
-      }
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
     }
     __syncthreads();  // all waves done reading the ring before the next item refills it
 
@@ -880,18 +923,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
   }
 }
 
-template <bool GATED, int WM, int WN, int WGM, int WGN>
+template <bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
+          bool ASKIP = false>
 static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
   constexpr int NTH = 64 * WGM * WGN;
   const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + ((NTH + 3) & ~3)) * sizeof(int32_t) +
-                     (size_t)kRing * (WGM * WM + WGN * WN) * 4 * 16;
-  auto kern = &ffn_tiled_dl_kernel<GATED, WM, WN, WGM, WGN>;
+                     (size_t)RING * (WGM * WM + WGN * WN) * (DK / 8) * 16;
+  auto kern = &ffn_tiled_dl_kernel<GATED, WM, WN, WGM, WGN, RING, DK, ASKIP>;
   if (lds > 64 * 1024) {
     hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (st != hipSuccess) return st;
   }
-  const int per_cu = lds > 80 * 1024 ? 1 : 2;
+  const int fit = (int)((160 * 1024) / lds);  // workgroups per CU that the LDS allows
+  const int per_cu = fit < 1 ? 1 : (fit > 4 ? 4 : fit);
   kern<<<dev.num_cus * per_cu, NTH, lds, stream>>>(p);
   return hipGetLastError();
 }
@@ -906,7 +951,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.rows == 0) return hipSuccess;
   // Which kernel takes which expert (decided per expert on the device from its row count):
   //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
-  //  - bf16/fp8 decode-sized batches (T*k < 32*E): bf16 weights go to the 128-row
+  //  - bf16/fp8 decode-sized batches (T*k < 32*E): bf16 weights go to the 64 x 128
   //    direct-to-LDS tiles for every expert; fp8 weights stream experts with <= 16 rows and
   //    tile the rest;
   //  - prefill-sized batches: experts with <= 16 rows stream, the rest take 256-row tiles.
@@ -932,10 +977,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.wdt == MOE_BF16) {
     if (stream_pass) st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled_dl<true, 64, 64, 2, 2>(tgu, dev, stream);
+      st = big ? launch_tiled_dl<true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled_dl<true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
     if (st == hipSuccess && stream_pass) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled_dl<false, 64, 64, 2, 2>(tdn, dev, stream);
+      st = big ? launch_tiled_dl<false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled_dl<false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);

@@ -719,12 +719,13 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 constexpr int kDK = 32;     // contraction step
 constexpr int kRing = 4;    // LDS ring depth
 
-// LDS image of a tile row of DK contraction elements (DK / 8 chunks of 16 bytes): chunk c of row
-// r sits at chunk c ^ x(r), x(r) = (r >> 2) & 3 for 4 chunks and (r >> 1) & 7 for 8 chunks, so
-// the 16 rows read by one fragment load (same chunk) fall on distinct banks.
-template <int DK>
+// LDS image of a tile row of CPR chunks of 16 bytes: chunk c of row r sits at chunk c ^ x(r),
+// x(r) = (r >> 2) & 3 for 4 chunks and (r >> 1) & 7 for 8 chunks, so that the 16 rows read by
+// one fragment load (same chunk) fall on distinct banks.
+template <int CPR>
 __device__ __forceinline__ int dswz(int row, int chunk) {
-  if constexpr (DK == 32) return row * 4 + (chunk ^ ((row >> 2) & 3));
+  static_assert(CPR == 4 || CPR == 8, "row width");
+  if constexpr (CPR == 4) return row * 4 + (chunk ^ ((row >> 2) & 3));
   else return row * 8 + (chunk ^ ((row >> 1) & 7));
 }
 
@@ -745,20 +746,30 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   wait_vmcnt_dyn_impl(n, std::make_integer_sequence<int, MAX + 1>{});
 }
 
-template <bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
+// WF: weight format, kBF16 or kFP8 (e4m3fn with fp32 scales per 128 x 128 block). fp8 weights
+// go to LDS as bytes and are widened to bf16 exactly after the fragment load; the MFMAs of one
+// 128-long contraction block accumulate into a partial tile that is then added to the
+// accumulator times the block's scale (identical dequantisation: the scale multiplies the
+// exact fp8 products' fp32 sum, never a rounded weight). fp8 needs DK = 64.
+template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
   static_assert(DK == 32 || DK == 64, "contraction step");
+  static_assert(WF == kBF16 || (WF == kFP8 && DK == 64), "weight format");
+  constexpr bool F8 = WF == kFP8;
+  constexpr int WB = F8 ? 1 : 2;                        // weight bytes per element
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
   constexpr int TM = WGM * WM, TN = WGN * WN;
   constexpr int MF = WM / 16, NF = WN / 16;
-  constexpr int CPR = DK / 8;                           // 16-byte chunks per tile row
-  constexpr int AI = TM * CPR / 64, BI = TN * CPR / 64; // 1 KB load instructions per step
+  constexpr int CPRA = DK * 2 / 16, CPRB = DK * WB / 16;  // 16-byte chunks per tile row
+  constexpr int AI = TM * CPRA / 64, BI = TN * CPRB / 64;  // 1 KB load instructions per step
   static_assert(BI % NW == 0 && (AI % NW == 0 || AI < NW), "loads must split evenly over waves");
   // A loads per wave: AI / NW each, or (short tiles) one each for the first AI waves
   constexpr int AIW = AI >= NW ? AI / NW : 1, BIW = BI / NW;
   constexpr int LPW = AIW + BIW;                        // most loads per wave per step
-  constexpr int STAGE = (TM + TN) * CPR;                // 16-byte chunks per ring slot
+  constexpr int ACH = TM * CPRA;                        // A chunks per ring slot
+  constexpr int STAGE = ACH + TN * CPRB;                // 16-byte chunks per ring slot
+  constexpr int KBS = 128 / DK;                         // steps per fp8 scale block
   extern __shared__ __align__(16) unsigned char smem[];
   const int Epad = (p.E + 1 + 3) & ~3;
   int32_t* pre = reinterpret_cast<int32_t*>(smem);
@@ -775,8 +786,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
   const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
   build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, 0x7fffffff, NT, offs, p.min_rows, TM);
   const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
-  const int nst = p.K / DK;  // K is a multiple of 64 on this path
-  const size_t wstride = (size_t)p.N * p.K;
+  const int nst = p.K / DK;  // K is a multiple of 64 (of 128 for fp8) on this path
+  const size_t wstride = (size_t)p.N * p.K * WB;  // bytes per expert matrix
+  const int NB = p.N / 128, KBn = p.K / 128;     // fp8 scale blocks
 
   for (int base = 0; base < total; base += gridDim.x) {
     const int item = xcd_round_item(base, total);
@@ -802,26 +814,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
     // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
     // issued: those LDS rows keep stale data, which only reaches accumulator rows that are
     // never stored (row r of the product depends on row r of A alone).
-    constexpr int RPI = 64 / CPR;  // tile rows per load instruction
+    constexpr int RPI = 64 / CPRA;  // tile rows per A load instruction
     int aiw = 0;
 #pragma unroll
     for (int i = 0; i < AIW; ++i)
       aiw += (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows)) ? 1 : 0;
     const int lpw = aiw + BIW;  // this wave's loads per step
 
-    // per-lane source of each of this wave's load instructions (element offsets at step 0)
+    // per-lane source of each of this wave's load instructions (byte offsets at step 0)
     size_t a_src[AIW], b_src[BIW];
     bool b_up[BIW];
 #pragma unroll
     for (int i = 0; i < AIW; ++i) {
       const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the A tile
-      const int r = q / CPR, c = dswz<DK>(r, q % CPR) - r * CPR;  // source chunk (XOR involution)
-      a_src[i] = (size_t)(r0 + min(r, nrows - 1)) * p.K + c * 8;
+      const int r = q / CPRA, c = dswz<CPRA>(r, q % CPRA) - r * CPRA;  // source chunk (XOR involution)
+      a_src[i] = ((size_t)(r0 + min(r, nrows - 1)) * p.K) * 2 + c * 16;
     }
 #pragma unroll
     for (int i = 0; i < BIW; ++i) {
       const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the B tile
-      const int t = q / CPR, c = dswz<DK>(t, q % CPR) - t * CPR;
+      const int t = q / CPRB, c = dswz<CPRB>(t, q % CPRB) - t * CPRB;
       int n;
       if constexpr (GATED) {
         const int blk = t / WN, qq = t % WN;
@@ -831,33 +843,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
         b_up[i] = false;
         n = c0 + t;
       }
-      b_src[i] = (size_t)e * wstride + (size_t)min(n, p.N - 1) * p.K + c * 8;
+      b_src[i] = (size_t)e * wstride + (size_t)min(n, p.N - 1) * p.K * WB + c * 16;
     }
-    const uint16_t* X = static_cast<const uint16_t*>(p.X);
-    const uint16_t* W1 = static_cast<const uint16_t*>(p.W1);
-    const uint16_t* W2 = GATED ? static_cast<const uint16_t*>(p.W2) : W1;
+    const uint8_t* X = static_cast<const uint8_t*>(p.X);
+    const uint8_t* W1 = static_cast<const uint8_t*>(p.W1);
+    const uint8_t* W2 = GATED ? static_cast<const uint8_t*>(p.W2) : W1;
 
     auto issue = [&](int st) __attribute__((always_inline)) {
       u32x4* slot = ring + (st % RING) * STAGE;
-      const size_t ko = (size_t)st * DK;
+      const size_t ka = (size_t)st * DK * 2, kb = (size_t)st * DK * WB;
 #pragma unroll
       for (int i = 0; i < AIW; ++i)
         if (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows))
           __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(X + a_src[i] + ko),
+              (const __attribute__((address_space(1))) void*)(X + a_src[i] + ka),
               (__attribute__((address_space(3))) void*)(slot + (wave + i * NW) * 64), 16, 0, 0);
 #pragma unroll
       for (int i = 0; i < BIW; ++i)
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)((b_up[i] ? W2 : W1) + b_src[i] + ko),
-            (__attribute__((address_space(3))) void*)(slot + TM * CPR + (wave + i * NW) * 64), 16, 0, 0);
+            (const __attribute__((address_space(1))) void*)((b_up[i] ? W2 : W1) + b_src[i] + kb),
+            (__attribute__((address_space(3))) void*)(slot + ACH + (wave + i * NW) * 64), 16, 0, 0);
     };
 
     f32x4 acc[MF][NF];
+    f32x4 part[F8 ? MF : 1][F8 ? NF : 1];  // fp8: this scale block's sums
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
       for (int jj = 0; jj < NF; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NF; ++jj) part[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // fp8 scale rows of this wave's columns (gate and up halves for the gated GEMM)
+    int sb0 = 0, sb1 = 0;
+    if constexpr (F8) {
+      const int n0 = GATED ? c0 + wn * (WN / 2) : c0 + wn * WN;
+      sb0 = (e * NB + min(n0 / 128, NB - 1)) * KBn;
+      sb1 = sb0;
+    }
 
 #pragma unroll
     for (int st = 0; st < RING - 1; ++st)
@@ -881,19 +907,45 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
         bf16x8 bfr[NF], afr[MF];
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
-          const u32x4 v = slot[TM * CPR + dswz<DK>(wn * WN + nf * 16 + (lane & 15), c)];
-          __builtin_memcpy(&bfr[nf], &v, 16);
+          const int row = wn * WN + nf * 16 + (lane & 15);
+          if constexpr (F8) {
+            // 8 fp8 of k = h*32 + (lane/16)*8: half of chunk c/2 of the 64-byte row
+            const uint2* half = reinterpret_cast<const uint2*>(slot + ACH + dswz<CPRB>(row, c >> 1));
+            bfr[nf] = fp8x8_to_bf16(half[c & 1]);
+          } else {
+            const u32x4 v = slot[ACH + dswz<CPRB>(row, c)];
+            __builtin_memcpy(&bfr[nf], &v, 16);
+          }
         }
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) {
-          const u32x4 v = slot[dswz<DK>(wm * WM + mf * 16 + (lane & 15), c)];
+          const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
           __builtin_memcpy(&afr[mf], &v, 16);
         }
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+          for (int nf = 0; nf < NF; ++nf) {
+            if constexpr (F8)
+              part[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], part[mf][nf], 0, 0, 0);
+            else
+              acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+          }
+      }
+      if constexpr (F8) {
+        if ((st + 1) % KBS == 0) {  // end of a 128-long scale block
+          const int kb = st / KBS;
+          const float s0 = p.S1[sb0 + kb];
+          const float s1 = GATED ? p.S2[sb1 + kb] : s0;
+#pragma unroll
+          for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+              const float sc = (GATED && nf >= NF / 2) ? s1 : s0;
+              acc[mf][nf] += sc * part[mf][nf];
+              part[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
       }
     }
     __syncthreads();  // all waves done reading the ring before the next item refills it
@@ -923,13 +975,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
   }
 }
 
-template <bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
+template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false>
 static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
   constexpr int NTH = 64 * WGM * WGN;
+  constexpr int WB = WF == kFP8 ? 1 : 2;
   const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + ((NTH + 3) & ~3)) * sizeof(int32_t) +
-                     (size_t)RING * (WGM * WM + WGN * WN) * (DK / 8) * 16;
-  auto kern = &ffn_tiled_dl_kernel<GATED, WM, WN, WGM, WGN, RING, DK, ASKIP>;
+                     (size_t)RING * (WGM * WM * DK * 2 + WGN * WN * DK * WB);
+  auto kern = &ffn_tiled_dl_kernel<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP>;
   if (lds > 64 * 1024) {
     hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -977,18 +1030,18 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.wdt == MOE_BF16) {
     if (stream_pass) st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled_dl<true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
+      st = big ? launch_tiled_dl<kBF16, true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
     if (st == hipSuccess && stream_pass) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled_dl<false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
+      st = big ? launch_tiled_dl<kBF16, false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream) : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
+    st = big ? launch_tiled_dl<kFP8, true, 64, 64, 2, 4, 4, 64>(tgu, dev, stream) : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
   if (st == hipSuccess) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream) : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
+    st = big ? launch_tiled_dl<kFP8, false, 64, 64, 2, 4, 4, 64>(tdn, dev, stream) : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
   return st;
 }
 

@@ -9,7 +9,9 @@ resident in HBM. Prints ONE JSON line on stdout (progress goes to stderr):
                token_dispatch_expert_amd.traffic; traffic = counter-measured HBM bytes when a
                profiles/ counter summary exists for the current kernel source, else null
   cpu_baseline the fp64 oracle timed on the host cores (a bounded sample of the workload)
-  breakdown    per-call time and roofline fraction of every step
+  breakdown    per-call time (mean, p10 / median / p90 over the timed passes, each pass starting
+               with the L2s and MALL flushed) and roofline fraction of every step; calls this short
+               include the host's launch gap, the kernel trace in profiles/ has the kernel times
 
 Workloads (--config, default c2 = the decode-shape Qwen3-235B-like layer): c1..c5 as in
 synth.CONFIGS. Other modes: --calibrate-copy runs a plain device copy of known size, the
@@ -160,9 +162,14 @@ def main() -> int:
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     perm_ws = moe.Workspace(moe.moe_permute_workspace_size(T, E, k), device=dev)
     ffn_ws = moe.Workspace(moe.moe_ffn_workspace_size(R, E, d, d_ff, act_t, w_t), device=dev)
-    acc = np.zeros(4)
+    # every timed pass starts with cold caches: reading 512 MiB evicts the L2s and the 256 MB MALL
+    # (a read, so that no dirty lines are left to be written back inside the timed calls)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    samples = []
     reps = max(args.steps, 1)
     for _ in range(reps):
+        flush.sum()
+        torch.cuda.synchronize()
         ev[0].record(stream)
         moe.moe_route(logits, k, out["topk_ids"], out["topk_gates"])
         ev[1].record(stream)
@@ -175,8 +182,10 @@ def main() -> int:
         moe.moe_combine(out["y_sorted"], out["flat_to_sorted"], out["topk_gates"], out["y"])
         ev[4].record(stream)
         torch.cuda.synchronize()
-        acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
-    t_us = acc / reps * 1e3  # microseconds per call
+        samples.append([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(4)])
+    samples = np.asarray(samples)  # [reps, 4] microseconds per call
+    t_us = samples.mean(axis=0)
+    pct = np.percentile(samples, [10, 50, 90], axis=0)
     a = 4 if cfg.act == "f32" else 2
     wb = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[cfg.w]
     sb = tr.fp8_scale_bytes(d, d_ff) if cfg.w == "fp8_e4m3fn" else 0
@@ -190,7 +199,9 @@ def main() -> int:
     breakdown = {}
     for i, name in enumerate(["route", "permute", "grouped_ffn", "combine"]):
         gbps = bytes_[name] / (t_us[i] * 1e-6) / 1e9
-        breakdown[name] = {"us": round(float(t_us[i]), 2), "alg_bytes": int(bytes_[name]),
+        breakdown[name] = {"us": round(float(t_us[i]), 2), "p10_us": round(float(pct[0, i]), 2),
+                           "median_us": round(float(pct[1, i]), 2), "p90_us": round(float(pct[2, i]), 2),
+                           "alg_bytes": int(bytes_[name]),
                            "GB_per_s": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     mfma_peak = MFMA_PEAK_TFLOPS["fp32" if cfg.act == "f32" else "bf16"]
     ffn_tflops = flops / (t_us[2] * 1e-6) / 1e12

@@ -717,6 +717,7 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 // The loading lanes pick their source addresses so that the linear LDS image is the swizzled
 // tile (see dswz).
 constexpr int kDK = 32;     // contraction step
+constexpr int kFp8DlMaxK = 65536;  // longest contraction of the fp8 direct-to-LDS kernel
 constexpr int kRing = 4;    // LDS ring depth
 
 // LDS image of a tile row of CPR chunks of 16 bytes: chunk c of row r sits at chunk c ^ x(r),
@@ -776,6 +777,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
   int32_t* offs = pre + Epad;
   int32_t* scan_tmp = offs + Epad;
   u32x4* ring = reinterpret_cast<u32x4*>(scan_tmp + ((NTH + 3) & ~3));   // [RING][STAGE]
+  // fp8: the current item's scales, [WGN column blocks][gate, up][K / 128], read from LDS in
+  // the loop (a global load there would make the compiler drain the prefetched steps)
+  float* sc_lds = reinterpret_cast<float*>(ring + RING * STAGE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -877,12 +881,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
 #pragma unroll
         for (int jj = 0; jj < NF; ++jj) part[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // fp8 scale rows of this wave's columns (gate and up halves for the gated GEMM)
-    int sb0 = 0, sb1 = 0;
+    // fp8: stage the scale rows of every wave column block (gate and up halves for the gated
+    // GEMM) in LDS; nothing is in flight here, the previous item ended with a full drain
     if constexpr (F8) {
-      const int n0 = GATED ? c0 + wn * (WN / 2) : c0 + wn * WN;
-      sb0 = (e * NB + min(n0 / 128, NB - 1)) * KBn;
-      sb1 = sb0;
+      for (int idx = tid; idx < WGN * 2 * KBn; idx += NTH) {
+        const int blk = idx / (2 * KBn), half = (idx / KBn) & 1, kb = idx % KBn;
+        const int n0 = GATED ? c0 + blk * (WN / 2) : c0 + blk * WN;
+        const size_t srow = ((size_t)e * NB + min(n0 / 128, NB - 1)) * KBn + kb;
+        sc_lds[idx] = (GATED && half) ? p.S2[srow] : (half ? 0.f : p.S1[srow]);
+      }
+      __syncthreads();
     }
 
 #pragma unroll
@@ -899,7 +907,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (st + RING - 1 < nst) issue(st + RING - 1);
       const u32x4* slot = ring + (st % RING) * STAGE;
 #pragma unroll
       for (int h = 0; h < DK / 32; ++h) {  // 32-wide MFMA contraction slices of the step
@@ -922,6 +929,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
           const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
           __builtin_memcpy(&afr[mf], &v, 16);
         }
+        // the next loads go out after this slice's fragment reads: DMA writes landing in LDS
+        // while the reads are in progress slow both down
+        if (h == 0 && st + RING - 1 < nst) issue(st + RING - 1);
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
@@ -935,8 +945,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       if constexpr (F8) {
         if ((st + 1) % KBS == 0) {  // end of a 128-long scale block
           const int kb = st / KBS;
-          const float s0 = p.S1[sb0 + kb];
-          const float s1 = GATED ? p.S2[sb1 + kb] : s0;
+          const float s0 = sc_lds[(wn * 2) * KBn + kb];
+          const float s1 = GATED ? sc_lds[(wn * 2 + 1) * KBn + kb] : s0;
 #pragma unroll
           for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
@@ -981,7 +991,8 @@ static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hip
   constexpr int NTH = 64 * WGM * WGN;
   constexpr int WB = WF == kFP8 ? 1 : 2;
   const size_t lds = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + ((NTH + 3) & ~3)) * sizeof(int32_t) +
-                     (size_t)RING * (WGM * WM * DK * 2 + WGN * WN * DK * WB);
+                     (size_t)RING * (WGM * WM * DK * 2 + WGN * WN * DK * WB) +
+                     (WF == kFP8 ? (size_t)WGN * 2 * (p.K / 128) * sizeof(float) : 0);
   auto kern = &ffn_tiled_dl_kernel<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP>;
   if (lds > 64 * 1024) {
     hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1021,6 +1032,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   TiledArgs tdn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
                 a.E, a.d_ff, a.d, a.rows, small};
   const bool stream_pass = small > 0;
+  // the fp8 direct-to-LDS kernel keeps an item's scale rows in LDS: 4 x 2 x K/128 floats
+  const bool fp8_dl = big && a.d <= kFp8DlMaxK && a.d_ff <= kFp8DlMaxK;
   hipError_t st = hipSuccess;
   if (a.act == MOE_F32) {
     st = launch_stream<kF32, kF32, 2, 1, 1, 4>(gu, dev, stream);
@@ -1038,10 +1051,14 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   }
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = big ? launch_tiled_dl<kFP8, true, 64, 64, 2, 4, 4, 64>(tgu, dev, stream) : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
+    st = fp8_dl ? launch_tiled_dl<kFP8, true, 64, 64, 2, 4, 4, 64>(tgu, dev, stream)
+                : (big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
+                       : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream));
   if (st == hipSuccess) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = big ? launch_tiled_dl<kFP8, false, 64, 64, 2, 4, 4, 64>(tdn, dev, stream) : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
+    st = fp8_dl ? launch_tiled_dl<kFP8, false, 64, 64, 2, 4, 4, 64>(tdn, dev, stream)
+                : (big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
+                       : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream));
   return st;
 }
 

@@ -30,6 +30,14 @@ oracle takes the readings listed below (each is also listed in the design notes)
   R7 (optional, off by default) h_round="bf16": h is rounded to the nearest bf16 between the
      two GEMMs, the rounding point of a bf16 implementation; tests use it as a second,
      tighter comparison next to the plain fp64 one.
+  R8 capacity factor (optional; same page, section 5, mitigation 1, and section 10, exercise
+     D): each expert keeps at most `capacity` assignments and the excess is dropped. The page
+     states capacity = C * tokens / E; with k > 1 the count is of assignments, so
+     capacity = ceil(C * T * k / E). The kept assignments of an expert are its first
+     `capacity` in flat order (the stable order of R3); a dropped assignment gets no row
+     (flat_to_sorted = -1) and adds nothing in the combine (the token passes the expert by,
+     the residual connection being outside the layer); the gates are not renormalised. The
+     factor is taken in percent, so the capacity is exact integer arithmetic.
 Everything is fp64 after an exact decode of the stored inputs; there is no blocking, fusion
 or reordering beyond the steps above. Library primitives used as steps: numpy argmax (first
 occurrence of the maximum), fp64 matrix products (BLAS) and exp.
@@ -116,25 +124,36 @@ def route(logits: np.ndarray, k: int):
 # ----------------------------------------------------------------------------------------
 # permute: count, exclusive scan, stable scatter, row copy (tutorial section 4, dispatch)
 # ----------------------------------------------------------------------------------------
-def permute(topk_ids: np.ndarray, E: int):
-    """Stable counting sort of the flat assignments i = t*k + j by expert id.
+def expert_capacity(T: int, E: int, k: int, factor_percent: int) -> int:
+    """capacity = ceil(C * T * k / E) assignments per expert (reading R8), with the factor
+    C given in percent (C = 1.25 -> 125) so that the value is exact integer arithmetic."""
+    return -(-(int(factor_percent) * T * k) // (100 * E))
 
-    Returns dict(counts int32 [E], offsets int32 [E+1], sorted_to_flat int32 [R],
-    flat_to_sorted int32 [R]). Reading R3."""
+
+def permute(topk_ids: np.ndarray, E: int, capacity: int | None = None):
+    """Stable counting sort of the flat assignments i = t*k + j by expert id (reading R3);
+    with a capacity, each expert keeps only its first `capacity` assignments (reading R8).
+
+    Returns dict(counts int32 [E] (kept assignments), offsets int32 [E+1],
+    sorted_to_flat int32 [offsets[E]], flat_to_sorted int32 [R], -1 where dropped)."""
     flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
     R = flat.size
     counts = np.zeros(E, dtype=np.int64)
     for i in range(R):
         counts[flat[i]] += 1
+    if capacity is not None:
+        counts = np.minimum(counts, capacity)
     offsets = np.zeros(E + 1, dtype=np.int64)
     for e in range(E):
         offsets[e + 1] = offsets[e] + counts[e]
     fill = offsets[:E].copy()
-    s2f = np.empty(R, dtype=np.int64)
-    f2s = np.empty(R, dtype=np.int64)
+    s2f = np.empty(int(offsets[E]), dtype=np.int64)
+    f2s = np.full(R, -1, dtype=np.int64)
     for i in range(R):
         e = flat[i]
         pos = fill[e]
+        if pos == offsets[e + 1]:
+            continue  # this expert is full: the assignment is dropped
         fill[e] += 1
         s2f[pos] = i
         f2s[i] = pos
@@ -210,13 +229,17 @@ def ffn(x_sorted: np.ndarray, offsets: np.ndarray, expert_weights, return_h: boo
 # combine (tutorial section 4, combine; reading R6)
 # ----------------------------------------------------------------------------------------
 def combine(y_sorted: np.ndarray, flat_to_sorted: np.ndarray, gates: np.ndarray) -> np.ndarray:
-    """y[t] = sum_j gates[t, j] * y_sorted[flat_to_sorted[t*k + j]], slot order, fp64."""
+    """y[t] = sum_j gates[t, j] * y_sorted[flat_to_sorted[t*k + j]], slot order, fp64; a
+    dropped slot (flat_to_sorted = -1, reading R8) adds nothing."""
     T, k = gates.shape
     y = np.zeros((T, y_sorted.shape[1]), dtype=np.float64)
     for t in range(T):
         acc = np.zeros(y_sorted.shape[1], dtype=np.float64)
         for j in range(k):
-            acc = acc + gates[t, j] * y_sorted[int(flat_to_sorted[t * k + j])]
+            pos = int(flat_to_sorted[t * k + j])
+            if pos < 0:
+                continue
+            acc = acc + gates[t, j] * y_sorted[pos]
         y[t] = acc
     return y
 
@@ -234,12 +257,12 @@ def make_weight_decoder(raw_weights, w_fmt: str):
 
 
 def layer(logits, x, x_fmt: str, raw_weights, w_fmt: str, k: int, return_h: bool = False,
-          h_round: str | None = None):
-    """The whole layer: route -> permute -> grouped FFN -> combine. Returns every
-    intermediate."""
+          h_round: str | None = None, capacity: int | None = None):
+    """The whole layer: route -> permute (optionally capped, R8) -> grouped FFN -> combine.
+    Returns every intermediate."""
     T, E = np.asarray(logits).shape
     ids, gates = route(logits, k)
-    p = permute(ids, E)
+    p = permute(ids, E, capacity)
     x_sorted = gather_rows(np.asarray(x), p["sorted_to_flat"], k)
     xs = decode_activations(x_sorted, x_fmt)
     dec = make_weight_decoder(raw_weights, w_fmt)

@@ -45,18 +45,31 @@ def tiny_case(T, d, E, k, d_ff, seed, fmt="f32", ties=False):
     return logits, x, W
 
 
-def brute_force_layer(logits, x, W, k):
+def kept_by_capacity(ids, E, cap):
+    """0/1 per flat assignment: kept iff fewer than `cap` earlier assignments (in flat order)
+    went to the same expert, from a stable argsort and a running count per group."""
+    flat = np.asarray(ids).reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    starts = np.searchsorted(flat[order], np.arange(E))
+    rank = np.empty(flat.size, dtype=np.int64)
+    rank[order] = np.arange(flat.size) - starts[flat[order]]
+    return rank < cap, rank
+
+
+def brute_force_layer(logits, x, W, k, cap=None):
     """Dense all-experts-masked evaluation written independently of the oracle: every expert
     runs on every token (einsum over the stored layouts), a 0/1 mask from a stable argsort
-    picks the top k, and the gates come from a full softmax renormalised over the top k."""
+    picks the top k, and the gates come from a full softmax renormalised over the top k. With
+    a capacity, slots beyond it (kept_by_capacity) are masked out of the sum."""
     l = logits.astype(np.float64)
     T, E = l.shape
     order = np.argsort(-l, axis=1, kind="stable")[:, :k]
     p = scipy.special.softmax(l, axis=1)
+    keep = np.ones((T, k), bool) if cap is None else kept_by_capacity(order, E, cap)[0].reshape(T, k)
     M = np.zeros((T, E))
     for t in range(T):
         sel = p[t, order[t]]
-        M[t, order[t]] = sel / sel.sum()
+        M[t, order[t]] = np.where(keep[t], sel / sel.sum(), 0.0)
     X = x.astype(np.float64)
     y = np.zeros_like(X)
     for e in range(E):
@@ -68,8 +81,8 @@ def brute_force_layer(logits, x, W, k):
     return y, order, M
 
 
-def run_oracle(logits, x, W, k):
-    return oracle.layer(logits, x, "f32", lambda e: W[e], "f32", k)
+def run_oracle(logits, x, W, k, cap=None):
+    return oracle.layer(logits, x, "f32", lambda e: W[e], "f32", k, capacity=cap)
 
 
 # ----------------------------------------------------------------------------------------
@@ -264,12 +277,75 @@ def check_bf16_value_rounding():
     assert np.array_equal(oracle.round_bf16_value(v.astype(np.float64)), ref)
 
 
+def check_capacity_formula():
+    # ceil(C * T * k / E) with C in percent, on values worked by hand
+    assert oracle.expert_capacity(512, 8, 1, 125) == 80      # the page's example, C = 1.25
+    assert oracle.expert_capacity(512, 8, 1, 100) == 64
+    assert oracle.expert_capacity(10, 3, 1, 100) == 4        # 10/3 rounds up
+    assert oracle.expert_capacity(128, 128, 8, 110) == 9     # 8.8 rounds up
+    assert oracle.expert_capacity(128, 128, 8, 100) == 8     # exact, no round-up
+    assert oracle.expert_capacity(64, 8, 2, 200) == 32
+
+
+def check_capacity_golden_example():
+    # the page's worked counts (section 5) under its typical C = 1.25: every expert keeps
+    # min(count, 80), the hot expert's load falls to 1.25x the balanced 64
+    g = _golden("load_imbalance_example.json")
+    E, T = g["experts"], g["tokens"]
+    counts = np.array(g["counts"])
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(7).shuffle(owner)
+    ids = owner.reshape(T, 1)
+    cap = oracle.expert_capacity(T, E, 1, 125)
+    p = oracle.permute(ids, E, cap)
+    assert p["counts"].tolist() == [80, 80, 78, 62, 48, 40, 31, 18]
+    assert p["offsets"][-1] == 437 and (p["flat_to_sorted"] < 0).sum() == 75
+    assert p["counts"].max() / g["balanced_per_expert"] == 1.25
+    kept, _ = kept_by_capacity(ids, E, cap)
+    assert np.array_equal(p["flat_to_sorted"] >= 0, kept)
+
+
+def check_capacity_vs_library():
+    for seed, (T, E, k) in enumerate([(13, 8, 2), (40, 5, 5), (64, 16, 1), (30, 4, 3)]):
+        logits, _, _ = tiny_case(T, 4, E, k, 4, 50 + seed, ties=True)
+        ids, _ = oracle.route(logits, k)
+        flat = ids.reshape(-1)
+        n = np.bincount(flat, minlength=E)
+        for cap in (0, 1, 2, 5, int(n.max()) - 1, int(n.max()), T):
+            if cap < 0:
+                continue
+            p = oracle.permute(ids, E, cap)
+            kept, rank = kept_by_capacity(ids, E, cap)
+            c = np.minimum(n, cap)
+            assert np.array_equal(p["counts"], c)
+            assert np.array_equal(p["offsets"], np.concatenate([[0], np.cumsum(c)]))
+            want = np.where(kept, np.concatenate([[0], np.cumsum(c)])[flat] + rank, -1)
+            assert np.array_equal(p["flat_to_sorted"], want)
+            assert np.array_equal(p["flat_to_sorted"][p["sorted_to_flat"]], np.arange(c.sum()))
+            if cap >= n.max():  # a capacity nobody reaches changes nothing
+                q = oracle.permute(ids, E)
+                assert all(np.array_equal(p[key], q[key]) for key in q)
+
+
+def check_capacity_brute_force_layer():
+    for seed, (T, d, E, k, d_ff) in enumerate([(20, 6, 4, 2, 8), (33, 5, 6, 3, 7), (16, 8, 3, 1, 4)]):
+        logits, x, W = tiny_case(T, d, E, k, d_ff, 300 + seed)
+        for cap in (0, 1, 3, 7, T):
+            ref, _, _ = brute_force_layer(logits, x, W, k, cap)
+            out = run_oracle(logits, x, W, k, cap)
+            if cap == 0:
+                assert np.all(out["y"] == 0.0) and out["offsets"][-1] == 0
+            else:
+                assert oracle.rel_max_err(out["y"], ref) < 1e-12, (seed, cap)
+
+
 CHECKS = [
     check_decode_bf16, check_decode_e4m3fn, check_route_vs_stable_argsort,
     check_route_special_cases, check_permute_vs_library, check_golden_load_example,
     check_golden_volume_example, check_swiglu_closed_form, check_brute_force_layer,
     check_identity_experts_and_gather, check_fp8_dequant_blocks, check_bf16_layer_decodes_inputs,
-    check_bf16_value_rounding,
+    check_bf16_value_rounding, check_capacity_formula, check_capacity_golden_example,
+    check_capacity_vs_library, check_capacity_brute_force_layer,
 ]
 
 
@@ -281,7 +357,8 @@ def test_oracle_pin(check):
 # ----------------------------------------------------------------------------------------
 # the pins must catch plausible mistakes planted in the oracle
 # ----------------------------------------------------------------------------------------
-_ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16")}
+_ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16",
+                                     "expert_capacity")}
 
 
 def _mut_route_tie_high(logits, k):
@@ -322,22 +399,52 @@ def _mut_route_no_max_shift_sign(logits, k):
     return ids, w / w.sum(1, keepdims=True)
 
 
-def _mut_permute_unstable(topk_ids, E):
-    p = _ORIG["permute"](topk_ids, E)
+def _mut_permute_unstable(topk_ids, E, capacity=None):
+    p = _ORIG["permute"](topk_ids, E, capacity)
     s2f = p["sorted_to_flat"].copy()
     for e in range(E):
         a, b = p["offsets"][e], p["offsets"][e + 1]
         s2f[a:b] = s2f[a:b][::-1]
-    f2s = np.empty_like(s2f)
+    f2s = np.full_like(p["flat_to_sorted"], -1)
     f2s[s2f] = np.arange(len(s2f))
     return dict(p, sorted_to_flat=s2f, flat_to_sorted=f2s.astype(np.int32))
 
 
-def _mut_permute_inclusive_scan(topk_ids, E):
-    p = _ORIG["permute"](topk_ids, E)
+def _mut_permute_inclusive_scan(topk_ids, E, capacity=None):
+    p = _ORIG["permute"](topk_ids, E, capacity)
     off = p["offsets"].copy()
     off[:-1] = off[1:]
     return dict(p, offsets=off)
+
+
+def _mut_permute_keep_last(topk_ids, E, capacity=None):
+    # a capacity that keeps each expert's last assignments instead of its first
+    if capacity is None:
+        return _ORIG["permute"](topk_ids, E)
+    R = np.asarray(topk_ids).size
+    p = _ORIG["permute"](np.asarray(topk_ids).reshape(-1)[::-1].reshape(R, 1), E, capacity)
+    f2s = p["flat_to_sorted"][::-1].copy()
+    s2f = np.full_like(p["sorted_to_flat"], 0)
+    s2f[f2s[f2s >= 0]] = np.nonzero(f2s >= 0)[0]
+    return dict(p, sorted_to_flat=s2f.astype(np.int32), flat_to_sorted=f2s.astype(np.int32))
+
+
+def _mut_permute_cap_plus_one(topk_ids, E, capacity=None):
+    return _ORIG["permute"](topk_ids, E, None if capacity is None else capacity + 1)
+
+
+def _mut_capacity_floor(T, E, k, factor_percent):
+    return (factor_percent * T * k) // (100 * E)
+
+
+def _mut_combine_keeps_dropped(y_sorted, flat_to_sorted, gates):
+    # a dropped slot's -1 used as an index (the last row) instead of being skipped
+    T, k = gates.shape
+    y = np.zeros((T, y_sorted.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            y[t] += gates[t, j] * y_sorted[int(flat_to_sorted[t * k + j])]
+    return y
 
 
 def _mut_ffn_silu_on_up(X, Wg, Wu, Wd, return_h=False):
@@ -387,6 +494,10 @@ MUTANTS = {
     "route_gate_sign": ("route", _mut_route_no_max_shift_sign),
     "permute_unstable": ("permute", _mut_permute_unstable),
     "permute_inclusive_scan": ("permute", _mut_permute_inclusive_scan),
+    "permute_keep_last": ("permute", _mut_permute_keep_last),
+    "permute_cap_plus_one": ("permute", _mut_permute_cap_plus_one),
+    "capacity_floor": ("expert_capacity", _mut_capacity_floor),
+    "combine_keeps_dropped": ("combine", _mut_combine_keeps_dropped),
     "ffn_silu_on_up": ("expert_ffn", _mut_ffn_silu_on_up),
     "ffn_sigmoid_only": ("expert_ffn", _mut_ffn_sigmoid_only),
     "ffn_down_untransposed": ("expert_ffn", _mut_ffn_down_untransposed),

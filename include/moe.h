@@ -101,6 +101,34 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, const int32_t* topk
                          int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_expert_capacity - ceil(C * T * k / E), the per-expert capacity for a capacity factor
+ * C = factor_percent / 100 (tutorial page, section 5, mitigation 1: capacity = C x tokens / E,
+ * here counting the T*k assignments; section 10, exercise D sweeps C from 1.0 to 2.0). Exact
+ * integer arithmetic; returns -1 if T < 0, E < 1, k < 1 or factor_percent < 0, and INT_MAX if
+ * the value does not fit an int.
+ */
+int moe_expert_capacity(int T, int E, int k, int factor_percent);
+
+/*
+ * moe_permute_capped - moe_permute with a capacity factor (same page, section 5, mitigation
+ * 1: the excess of an over-full expert is dropped and passes the expert by). Each expert
+ * keeps its first `capacity` assignments in flat order (capacity >= 0, else
+ * MOE_ERR_INVALID_ARG):
+ *   counts         [E] out: kept rows per expert, min(assignments, capacity).
+ *   offsets        [E+1] out: exclusive scan of counts; offsets[E] = kept rows <= T*k.
+ *   sorted_to_flat entries [0, offsets[E]) are written, the rest are left untouched.
+ *   flat_to_sorted [T*k] out: the row of each kept assignment, -1 for a dropped one.
+ *   x_sorted       rows [0, offsets[E]) are written.
+ * moe_grouped_ffn then works on the kept rows only (it takes its rows from offsets) and
+ * moe_combine skips the dropped slots. Other arguments as moe_permute.
+ */
+moe_status_t moe_permute_capped(const void* x, moe_dtype_t x_dtype, const int32_t* topk_ids,
+                                int T, int E, int k, int d, int capacity, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_to_flat,
+                                int32_t* flat_to_sorted, void* x_sorted, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace moe_grouped_ffn needs (holds the SwiGLU activations h [rows, d_ff] in
  * act_dtype between the two GEMMs, plus a small schedule). */
 size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_dtype,
@@ -144,7 +172,8 @@ moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const 
  * sum (tutorial page, section 4, combine).
  *
  *   y[t] = sum_{j=0..k-1} topk_gates[t, j] * y_sorted[flat_to_sorted[t*k + j]]
- *   summed in fp32 in slot order j = 0..k-1.
+ *   summed in fp32 in slot order j = 0..k-1. A slot whose flat_to_sorted entry is negative (an
+ *   assignment dropped by moe_permute_capped) adds nothing; so does one at or past T*k.
  *
  *   y_sorted [T*k, d] fp32; flat_to_sorted [T*k] int32; topk_gates [T, k] fp32;
  *   y [T, d] fp32 out. Requires d a multiple of 4.
@@ -169,6 +198,20 @@ moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype
                        int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
                        float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * moe_layer_capped - moe_layer with moe_permute_capped in place of moe_permute (each expert
+ * keeps at most `capacity` assignments; see moe_expert_capacity). Dropped slots add nothing to
+ * y; the gates are not renormalised. The workspace is that of moe_layer.
+ */
+moe_status_t moe_layer_capped(const float* logits, const void* x, moe_dtype_t act_dtype, int T,
+                              int E, int k, int d, int d_ff, int capacity, const void* w_gate,
+                              const void* w_up, const void* w_down, moe_dtype_t w_dtype,
+                              const float* s_gate, const float* s_up, const float* s_down,
+                              int32_t* topk_ids, float* topk_gates, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                              void* x_sorted, float* y_sorted, float* y, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

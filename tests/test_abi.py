@@ -23,7 +23,7 @@ MIS = 0x7F0000000002  # misaligned
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:moe_status_t|size_t|const char\s*\*)\s*(moe_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|size_t|int|const char\s*\*)\s*(moe_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -84,6 +84,31 @@ def test_permute_rejects_bad_arguments(lib):
     assert call(x=None, ws=None) == B.MOE_ERR_INVALID_ARG
     assert call(xs=MIS, ws=None) == B.MOE_ERR_INVALID_ARG
     assert call(k=9, ws=None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_capacity_entry_points(lib):
+    cap = lib.moe_expert_capacity
+    assert cap(512, 8, 1, 125) == 80          # the tutorial's worked counts at C = 1.25
+    assert cap(10, 3, 1, 100) == 4 and cap(128, 128, 8, 110) == 9 and cap(128, 128, 8, 100) == 8
+    assert cap(0, 8, 2, 150) == 0
+    assert cap(-1, 8, 2, 100) == -1 and cap(8, 0, 2, 100) == -1 and cap(8, 8, 0, 100) == -1
+    assert cap(8, 8, 2, -5) == -1
+    assert cap(1 << 30, 1, 1, 1000) == 2**31 - 1  # saturates
+    T, E, k, d = 64, 8, 2, 128
+    ws = lib.moe_permute_workspace_size(T, E, k)
+    a = [P, B.MOE_BF16, P2, T, E, k, d, 5, P3, P3, P3, P3, P, P2, ws, None]
+    a[7] = -1
+    assert lib.moe_permute_capped(*a) == B.MOE_ERR_INVALID_ARG
+    a[7] = 5
+    a[-3] = None
+    assert lib.moe_permute_capped(*a) == B.MOE_ERR_WORKSPACE
+    d_ff = 256
+    need = lib.moe_layer_workspace_size(T, E, k, d, d_ff, B.MOE_BF16, B.MOE_BF16)
+    la = [P, P2, B.MOE_BF16, T, E, k, d, d_ff, -3, P, P2, P3, B.MOE_BF16, None, None, None,
+          P, P2, P3, P, P2, P3, P, P2, P3, P, need, None]
+    assert lib.moe_layer_capped(*la) == B.MOE_ERR_INVALID_ARG
+    la[8], la[-2] = 4, need - 16
+    assert lib.moe_layer_capped(*la) == B.MOE_ERR_WORKSPACE
 
 
 def test_ffn_rejects_bad_arguments(lib):

@@ -1,0 +1,112 @@
+"""GPU parity of the capacity factor ("Expert Parallelism" tutorial page, section 5,
+mitigation 1; section 10, exercise D): moe_layer_capped / moe_permute_capped against the
+oracle with the same capacity, on the single-workgroup (T*k <= 8192) and the tiled
+(T*k > 8192) permutation paths. Routing, counts, offsets and both maps are compared bit for
+bit; outputs within the format's tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import oracle
+import synth
+import token_dispatch_expert_amd as moe
+from token_dispatch_expert_amd.binding import layer_buffers
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return H.require_gpu()
+
+
+def run_capped(cfg, logits, x, W, dev, cap):
+    lg = torch.from_numpy(logits).to(dev)
+    xd = H.to_dev(x, cfg.act, dev)
+    out = layer_buffers(cfg.T, cfg.E, cfg.k, cfg.d, H.ACT_TORCH[cfg.act], device=dev)
+    for t in out.values():  # poison: rows past the kept ones must not be needed
+        if t.dtype in (torch.float32, torch.bfloat16):
+            t.fill_(float("nan"))
+        else:
+            t.fill_(-7)
+    ws = moe.Workspace(moe.moe_layer_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff,
+                                                    H.ACT_TORCH[cfg.act], H.W_TORCH[cfg.w]), device=dev)
+    moe.moe_layer(lg, xd, W.gate, W.up, W.down, cfg.k, out, ws, capacity=cap, **W.kwargs())
+    torch.cuda.synchronize()
+    return {n: H.to_host(t) for n, t in out.items()}
+
+
+def check_capped(cfg, got, ref, cap):
+    kept = int(ref["offsets"][-1])
+    assert int(got["offsets"][-1]) == kept
+    for n in ("topk_ids", "counts", "offsets", "flat_to_sorted"):
+        assert np.array_equal(got[n], ref[n]), n
+    assert np.array_equal(got["sorted_to_flat"][:kept], ref["sorted_to_flat"]), "sorted_to_flat"
+    assert np.array_equal(got["x_sorted"][:kept], ref["x_sorted"]), "x_sorted"
+    tol = H.TOL[cfg.w]
+    assert np.all(np.isfinite(got["y"]))
+    # a token whose every slot was dropped gets exactly 0; the others are compared with the
+    # tolerance over those rows only (the rms over a mostly-zero y would not measure anything)
+    live = (ref["flat_to_sorted"].reshape(cfg.T, cfg.k) >= 0).any(axis=1)
+    assert np.all(got["y"][~live] == 0.0), "a token with every slot dropped is not zero"
+    if kept:
+        e_ys = oracle.rel_max_err(got["y_sorted"][:kept], ref["y_sorted"])
+        e_y = oracle.rel_max_err(got["y"][live], ref["y"][live])
+        print(f"capacity {cap}: kept {kept}/{cfg.T * cfg.k} ({live.sum()} tokens), "
+              f"y_sorted err {e_ys:.3e}, y err {e_y:.3e}", flush=True)
+        assert e_ys <= tol and e_y <= tol
+
+
+@pytest.mark.parametrize("T,E,k,d,d_ff,act,w", [
+    (300, 16, 4, 256, 256, "bf16", "bf16"),    # single-workgroup permutation
+    (3000, 64, 4, 128, 128, "f32", "f32"),     # T*k = 12000: tiled permutation
+])
+def test_layer_with_capacity(dev, T, E, k, d, d_ff, act, w):
+    cfg = synth.tiny_config(T=T, d=d, E=E, k=k, d_ff=d_ff, act=act, w=w, zipf_s=1.2, seed=21)
+    logits, x = synth.make_routing_inputs(cfg)
+    W = H.DeviceWeights(cfg, dev)
+    caps = [0, 1] + [oracle.expert_capacity(T, E, k, p) for p in (100, 125, 150, 200)] + [T]
+    for cap in caps:
+        assert moe.moe_expert_capacity(T, E, k, 125) == oracle.expert_capacity(T, E, k, 125)
+        got = run_capped(cfg, logits, x, W, dev, cap)
+        ref = oracle.layer(logits, x, act, W.raw, w, k, capacity=cap)
+        check_capped(cfg, got, ref, cap)
+
+
+def test_permute_capacity_prefill_size(dev):
+    """Routing and maps only, at the 65,536-assignment prefill size."""
+    cfg = synth.CONFIGS["c4"]
+    logits, _ = synth.make_routing_inputs(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    ids = torch.from_numpy(oracle.route(logits, k)[0]).to(dev)
+    x = torch.zeros((T, 8), dtype=torch.bfloat16, device=dev)
+    ws = moe.Workspace(moe.moe_permute_workspace_size(T, E, k), device=dev)
+    for p in (100, 150):
+        cap = moe.moe_expert_capacity(T, E, k, p)
+        out = layer_buffers(T, E, k, 8, torch.bfloat16, device=dev)
+        moe.moe_permute(x, ids, E, out["counts"], out["offsets"], out["sorted_to_flat"],
+                        out["flat_to_sorted"], out["x_sorted"], ws, capacity=cap)
+        torch.cuda.synchronize()
+        ref = oracle.permute(ids.cpu().numpy(), E, cap)
+        kept = int(ref["offsets"][-1])
+        print(f"C = {p / 100}: capacity {cap}, dropped {T * k - kept} of {T * k}", flush=True)
+        for n in ("counts", "offsets", "flat_to_sorted"):
+            assert np.array_equal(out[n].cpu().numpy(), ref[n]), n
+        assert np.array_equal(out["sorted_to_flat"][:kept].cpu().numpy(), ref["sorted_to_flat"])
+
+
+def test_combine_skips_dropped_slots(dev):
+    rng = np.random.default_rng(5)
+    T, k, d = 37, 3, 64
+    R = T * k
+    ys = rng.standard_normal((R, d)).astype(np.float32)
+    f2s = rng.permutation(R).astype(np.int32)
+    f2s[rng.random(R) < 0.3] = -1
+    gates = rng.random((T, k)).astype(np.float32)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    moe.moe_combine(torch.from_numpy(ys).to(dev), torch.from_numpy(f2s).to(dev),
+                    torch.from_numpy(gates).to(dev), y)
+    torch.cuda.synchronize()
+    ref = oracle.combine(ys.astype(np.float64), f2s, gates.astype(np.float64))
+    assert oracle.rel_max_err(y.cpu().numpy(), ref) <= 1e-6

@@ -26,7 +26,7 @@ _DTYPE_ENUM = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16,
 ENTRY_POINTS = (
     "moe_status_string", "moe_route", "moe_permute_workspace_size", "moe_permute",
     "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
-    "moe_layer",
+    "moe_layer", "moe_expert_capacity", "moe_permute_capped", "moe_layer_capped",
 )
 
 _lib = None
@@ -63,6 +63,10 @@ def load_library(path: str | None = None):
         "moe_layer_workspace_size": ([I, I, I, I, I, I, I], S),
         "moe_layer": ([P, P, I, I, I, I, I, I, P, P, P, I, P, P, P,
                        P, P, P, P, P, P, P, P, P, P, S, P], I),
+        "moe_expert_capacity": ([I, I, I, I], I),
+        "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
+        "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
+                              P, P, P, P, P, P, P, P, P, P, S, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -155,7 +159,8 @@ def moe_route(logits, k: int, topk_ids, topk_gates, counts=None, stream=None):
 
 
 def moe_permute(x, topk_ids, E: int, counts, offsets, sorted_to_flat, flat_to_sorted, x_sorted,
-                workspace: Workspace, stream=None):
+                workspace: Workspace, stream=None, capacity: int | None = None):
+    """capacity (optional): most kept assignments per expert (moe_permute_capped)."""
     T, d = x.shape
     k = topk_ids.shape[1]
     R = T * k
@@ -165,10 +170,19 @@ def moe_permute(x, topk_ids, E: int, counts, offsets, sorted_to_flat, flat_to_so
     _need(sorted_to_flat, torch.int32, (R,), "sorted_to_flat")
     _need(flat_to_sorted, torch.int32, (R,), "flat_to_sorted")
     _need(x_sorted, x.dtype, (R, d), "x_sorted")
-    _check(load_library().moe_permute(
-        _ptr(x), _dt(x, "x"), _ptr(topk_ids), T, E, k, d, _ptr(counts), _ptr(offsets),
-        _ptr(sorted_to_flat), _ptr(flat_to_sorted), _ptr(x_sorted), workspace.ptr,
-        workspace.nbytes, _stream(stream)))
+    lib = load_library()
+    head = (_ptr(x), _dt(x, "x"), _ptr(topk_ids), T, E, k, d)
+    tail = (_ptr(counts), _ptr(offsets), _ptr(sorted_to_flat), _ptr(flat_to_sorted),
+            _ptr(x_sorted), workspace.ptr, workspace.nbytes, _stream(stream))
+    if capacity is None:
+        _check(lib.moe_permute(*head, *tail))
+    else:
+        _check(lib.moe_permute_capped(*head, int(capacity), *tail))
+
+
+def moe_expert_capacity(T: int, E: int, k: int, factor_percent: int) -> int:
+    """ceil(C * T * k / E) for C = factor_percent / 100 (exact; -1 for invalid sizes)."""
+    return load_library().moe_expert_capacity(T, E, k, int(factor_percent))
 
 
 def _weights(w_gate, w_up, w_down, s_gate, s_up, s_down):
@@ -214,9 +228,10 @@ def moe_combine(y_sorted, flat_to_sorted, topk_gates, y, stream=None):
 
 
 def moe_layer(logits, x, w_gate, w_up, w_down, k: int, out: dict, workspace: Workspace,
-              s_gate=None, s_up=None, s_down=None, stream=None):
+              s_gate=None, s_up=None, s_down=None, stream=None, capacity: int | None = None):
     """out holds the caller's buffers: topk_ids, topk_gates, counts, offsets, sorted_to_flat,
-    flat_to_sorted, x_sorted, y_sorted, y (see `layer_buffers`)."""
+    flat_to_sorted, x_sorted, y_sorted, y (see `layer_buffers`). capacity (optional): most
+    kept assignments per expert (moe_layer_capped)."""
     T, E = logits.shape
     _need(logits, torch.float32, (T, E), "logits")
     Ew, d, d_ff, w_dt = _weights(w_gate, w_up, w_down, s_gate, s_up, s_down)
@@ -231,12 +246,16 @@ def moe_layer(logits, x, w_gate, w_up, w_down, k: int, out: dict, workspace: Wor
     for n, (dt, shp) in shapes.items():
         _need(out[n], dt, shp, n)
     o = out
-    _check(load_library().moe_layer(
-        _ptr(logits), _ptr(x), _dt(x, "x"), T, E, k, d, d_ff, _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), w_dt, _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(o["topk_ids"]),
-        _ptr(o["topk_gates"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted_to_flat"]),
-        _ptr(o["flat_to_sorted"]), _ptr(o["x_sorted"]), _ptr(o["y_sorted"]), _ptr(o["y"]),
-        workspace.ptr, workspace.nbytes, _stream(stream)))
+    lib = load_library()
+    head = (_ptr(logits), _ptr(x), _dt(x, "x"), T, E, k, d, d_ff)
+    tail = (_ptr(w_gate), _ptr(w_up), _ptr(w_down), w_dt, _ptr(s_gate), _ptr(s_up), _ptr(s_down),
+            _ptr(o["topk_ids"]), _ptr(o["topk_gates"]), _ptr(o["counts"]), _ptr(o["offsets"]),
+            _ptr(o["sorted_to_flat"]), _ptr(o["flat_to_sorted"]), _ptr(o["x_sorted"]),
+            _ptr(o["y_sorted"]), _ptr(o["y"]), workspace.ptr, workspace.nbytes, _stream(stream))
+    if capacity is None:
+        _check(lib.moe_layer(*head, *tail))
+    else:
+        _check(lib.moe_layer_capped(*head, int(capacity), *tail))
 
 
 def layer_buffers(T: int, E: int, k: int, d: int, act_dtype, device="cuda") -> dict:

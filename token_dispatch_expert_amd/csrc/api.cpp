@@ -163,12 +163,30 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, const int32_t* topk
                          int E, int k, int d, int32_t* counts, int32_t* offsets,
                          int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_permute_capped(x, x_dtype, topk_ids, T, E, k, d, INT_MAX, counts, offsets,
+                            sorted_to_flat, flat_to_sorted, x_sorted, workspace, workspace_bytes,
+                            stream);
+}
+
+int moe_expert_capacity(int T, int E, int k, int factor_percent) {
+  if (T < 0 || E < 1 || k < 1 || factor_percent < 0) return -1;
+  const long long num = (long long)factor_percent * T * k, den = 100LL * E;
+  const long long cap = (num + den - 1) / den;
+  return cap > INT_MAX ? INT_MAX : (int)cap;
+}
+
+moe_status_t moe_permute_capped(const void* x, moe_dtype_t x_dtype, const int32_t* topk_ids,
+                                int T, int E, int k, int d, int capacity, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_to_flat,
+                                int32_t* flat_to_sorted, void* x_sorted, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
   moe_status_t s = check_permute(x, x_dtype, topk_ids, T, E, k, d, counts, offsets,
                                  sorted_to_flat, flat_to_sorted, x_sorted, workspace,
                                  workspace_bytes);
   if (s != MOE_OK) return s;
-  return hip_status(moe::launch_permute(x, act_bytes(x_dtype), topk_ids, T, E, k, d, counts,
-                                        offsets, sorted_to_flat, flat_to_sorted, x_sorted,
+  return hip_status(moe::launch_permute(x, act_bytes(x_dtype), topk_ids, T, E, k, d, capacity,
+                                        counts, offsets, sorted_to_flat, flat_to_sorted, x_sorted,
                                         static_cast<int32_t*>(workspace),
                                         static_cast<hipStream_t>(stream)));
 }
@@ -213,14 +231,15 @@ size_t moe_layer_workspace_size(int T, int E, int k, int d, int d_ff, moe_dtype_
          moe_ffn_workspace_size(T * k, E, d, d_ff, act_dtype, w_dtype);
 }
 
-moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype, int T, int E,
-                       int k, int d, int d_ff, const void* w_gate, const void* w_up,
+moe_status_t moe_layer_capped(const float* logits, const void* x, moe_dtype_t act_dtype, int T,
+                              int E, int k, int d, int d_ff, int capacity, const void* w_gate, const void* w_up,
                        const void* w_down, moe_dtype_t w_dtype, const float* s_gate,
                        const float* s_up, const float* s_down, int32_t* topk_ids,
                        float* topk_gates, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
                        float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
                        void* stream) {
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
   moe_status_t s = check_route(logits, T, E, k, topk_ids, topk_gates, nullptr);
   if (s != MOE_OK) return s;
   const size_t ws_perm = moe_permute_workspace_size(T, E, k);
@@ -243,7 +262,7 @@ moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype
   if (moe::device_info(&dev) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_route(logits, T, E, k, topk_ids, topk_gates, nullptr, st) != hipSuccess)
     return MOE_ERR_HIP;
-  if (moe::launch_permute(x, act_bytes(act_dtype), topk_ids, T, E, k, d, counts, offsets,
+  if (moe::launch_permute(x, act_bytes(act_dtype), topk_ids, T, E, k, d, capacity, counts, offsets,
                           sorted_to_flat, flat_to_sorted, x_sorted,
                           reinterpret_cast<int32_t*>(wsb), st) != hipSuccess)
     return MOE_ERR_HIP;
@@ -251,6 +270,20 @@ moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype
                  w_dtype, s_gate, s_up, s_down, y_sorted, wsb + ws_perm};
   if (moe::launch_grouped_ffn(a, dev, st) != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y, st));
+}
+
+moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype, int T, int E,
+                       int k, int d, int d_ff, const void* w_gate, const void* w_up,
+                       const void* w_down, moe_dtype_t w_dtype, const float* s_gate,
+                       const float* s_up, const float* s_down, int32_t* topk_ids,
+                       float* topk_gates, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                       float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return moe_layer_capped(logits, x, act_dtype, T, E, k, d, d_ff, INT_MAX, w_gate, w_up, w_down,
+                          w_dtype, s_gate, s_up, s_down, topk_ids, topk_gates, counts, offsets,
+                          sorted_to_flat, flat_to_sorted, x_sorted, y_sorted, y, workspace,
+                          workspace_bytes, stream);
 }
 
 }  // extern "C"

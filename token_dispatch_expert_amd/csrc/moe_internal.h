@@ -46,10 +46,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 
 // workspace: n_tiles * E int32 (per-tile histograms, then per-tile bases)
 size_t permute_workspace_ints(int T, int E, int k);
+// cap: most kept assignments per expert (INT_MAX: no capacity limit)
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int T, int E, int k,
-                          int d, int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat,
-                          int32_t* flat_to_sorted, void* x_sorted, int32_t* ws,
-                          hipStream_t stream);
+                          int d, int cap, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                          int32_t* ws, hipStream_t stream);
 
 struct FfnArgs {
   const void* x_sorted;

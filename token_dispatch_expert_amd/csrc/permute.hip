@@ -6,6 +6,12 @@
 // the flat index i = t*k + j, so within an expert rows appear in token order and the
 // permutation is unique (the k experts of one token are distinct).
 //
+// Capacity factor ("Expert Parallelism" tutorial page, section 5, mitigation 1): with a
+// capacity c, an expert keeps its first c assignments in flat order; the counts and offsets
+// are those of the kept rows, a dropped assignment gets flat_to_sorted = -1 and no row.
+// Every position is still ranked among all of the expert's assignments, and a position at or
+// past the expert's capped end is dropped, so capping costs nothing extra.
+//
 // Batches of more than kSmallR assignments take four launches, none using float atomics, all
 // deterministic (smaller batches use one workgroup for the first three, see
 // permute_small_kernel):
@@ -47,7 +53,7 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
 constexpr int kScanThreads = 1024;  // >= MOE_MAX_EXPERTS
 
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ ws,
-                                                                    int n_tiles, int E, int R,
+                                                                    int n_tiles, int E, int cap,
                                                                     int32_t* __restrict__ counts,
                                                                     int32_t* __restrict__ offsets) {
   __shared__ int32_t sc[kScanThreads];
@@ -68,6 +74,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
         }
       }
     }
+    total = min(total, cap);  // kept assignments (capacity factor)
     counts[e] = total;
   }
   sc[threadIdx.x] = total;
@@ -83,18 +90,23 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
     offsets[e] = excl;
     for (int t = 0; t < n_tiles; ++t) ws[(size_t)t * E + e] += excl;
   }
-  if (threadIdx.x == 0) offsets[E] = R;
+  if (threadIdx.x == 0) offsets[E] = sc[kScanThreads - 1];
 }
 
 __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __restrict__ ids,
                                                              int R, int E, int nbits,
                                                              const int32_t* __restrict__ ws,
+                                                             const int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ s2f,
                                                              int32_t* __restrict__ f2s) {
-  extern __shared__ int32_t run[];
+  extern __shared__ int32_t run[];  // [E] running positions, then [E] end of each expert
+  int32_t* lim = run + E;
   const int lane = threadIdx.x;
   const int32_t* bases = ws + (size_t)blockIdx.x * E;
-  for (int e = lane; e < E; e += kWave) run[e] = bases[e];
+  for (int e = lane; e < E; e += kWave) {
+    run[e] = bases[e];
+    lim[e] = offsets[e + 1];
+  }
   __syncthreads();
   const int base = blockIdx.x * kPermuteTile;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -109,9 +121,10 @@ __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __re
       same &= bit ? ones : ~ones;
     }
     if (valid) {
+      // positions at or past the expert's end are beyond its capacity: dropped
       const int pos = run[e] + __popcll(same & lower);
-      s2f[pos] = i;
-      f2s[i] = pos;
+      if (pos < lim[e]) s2f[pos] = i;
+      f2s[i] = pos < lim[e] ? pos : -1;
     }
     __syncthreads();
     // the highest lane of each group of equal experts advances that expert's base
@@ -129,7 +142,8 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   const uint4* src = x + (size_t)t * vec_per_row;
   for (int v = threadIdx.x; v < vec_per_row; v += blockDim.x) {
     const uint4 val = src[v];
-    for (int j = 0; j < k; ++j) xs[(size_t)pos[j] * vec_per_row + v] = val;
+    for (int j = 0; j < k; ++j)
+      if (pos[j] >= 0) xs[(size_t)pos[j] * vec_per_row + v] = val;  // -1: dropped slot
   }
 }
 
@@ -143,7 +157,7 @@ constexpr int kSmallChunks = 8;  // 64-entry chunks per wave -> R <= 16 * 8 * 64
 constexpr int kSmallR = kSmallWaves * kSmallChunks * kWave;
 
 __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int nbits, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ ids, int R, int E, int nbits, int cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ s2f, int32_t* __restrict__ f2s) {
   extern __shared__ int32_t sm[];
   int32_t* wc = sm;                                  // [16][E] per-wave counts, then bases
@@ -184,6 +198,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
       wc[w * E + tid] = total;
       total += t;
     }
+    total = min(total, cap);  // kept assignments (capacity factor)
     counts[tid] = total;
   }
   sc[tid] = total;
@@ -199,23 +214,26 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
     offsets[tid] = base;
     for (int w = 0; w < kSmallWaves; ++w) wc[w * E + tid] += base;
   }
-  if (tid == 0) offsets[E] = R;
+  if (tid == 0) offsets[E] = sc[kSmallWaves * kWave - 1];
   __syncthreads();
+  // sc[e] (inclusive scan) is the end of expert e's rows: positions at or past it are beyond
+  // the capacity and dropped
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c) {
     const int i = lo + c * kWave + lane;
     if (i < hi) {
       const int pos = mine[exp_[c]] + rank[c];
-      s2f[pos] = i;
-      f2s[i] = pos;
+      const bool keep = pos < sc[exp_[c]];
+      if (keep) s2f[pos] = i;
+      f2s[i] = keep ? pos : -1;
     }
   }
 }
 
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int T, int E, int k,
-                          int d, int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat,
-                          int32_t* flat_to_sorted, void* x_sorted, int32_t* ws,
-                          hipStream_t stream) {
+                          int d, int cap, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                          int32_t* ws, hipStream_t stream) {
   const int R = T * k;
   const int n_tiles = (R + kPermuteTile - 1) / kPermuteTile;
   const size_t lds = (size_t)E * sizeof(int32_t);
@@ -230,8 +248,9 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
       if (st != hipSuccess) return st;
     }
-    permute_small_kernel<<<1, kSmallWaves * kWave, slds, stream>>>(ids, R, E, nbits, counts, offsets,
-                                                                   sorted_to_flat, flat_to_sorted);
+    permute_small_kernel<<<1, kSmallWaves * kWave, slds, stream>>>(ids, R, E, nbits, cap, counts,
+                                                                   offsets, sorted_to_flat,
+                                                                   flat_to_sorted);
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
     permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,
@@ -243,11 +262,11 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
   }
-  permute_scan_kernel<<<1, kScanThreads, 0, stream>>>(ws, n_tiles, E, R, counts, offsets);
+  permute_scan_kernel<<<1, kScanThreads, 0, stream>>>(ws, n_tiles, E, cap, counts, offsets);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess || n_tiles == 0) return st;
-  permute_rank_kernel<<<n_tiles, kWave, lds, stream>>>(ids, R, E, nbits, ws, sorted_to_flat,
-                                                        flat_to_sorted);
+  permute_rank_kernel<<<n_tiles, kWave, 2 * lds, stream>>>(ids, R, E, nbits, ws, offsets,
+                                                            sorted_to_flat, flat_to_sorted);
   st = hipGetLastError();
   if (st != hipSuccess) return st;
   permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,

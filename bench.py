@@ -68,6 +68,197 @@ def calibrate_copy(steps: int) -> None:
     log(f"copied {COPY_CAL_BYTES} bytes x {steps}")
 
 
+def _time_calls(fn, reps: int, warmup: int = 2) -> list:
+    """Per-call times in microseconds of fn() on the current stream (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1e3)
+    return out
+
+
+def expert_time_sweep(args) -> int:
+    """Expert-time profile of moe_grouped_ffn (the makespan abstract's max-affine model on this
+    GPU): G active experts with n rows each, every other expert empty, at the decode (d=4096,
+    d_ff=1536, E=128) and DeepSeek-V3 (d=7168, d_ff=2048, E=256) shapes, bf16. Fits
+    t = max(a + b*G, c + beta*N) (N = G*n rows) and reports n* = b / beta, the row count where
+    an expert's time stops being its weight streaming."""
+    import numpy as np
+    import torch
+    import token_dispatch_expert_amd as moe
+    dev = torch.device("cuda:0")
+    ns = [1, 2, 4, 8, 16, 32, 64, 128, 192, 256, 384, 512, 768, 1024, 2048]
+    Gs = [1, 4, 16, 64]
+    shapes = [("decode Qwen3-like", 4096, 1536, 128), ("DeepSeek-V3-like", 7168, 2048, 256)]
+    result = {"metric": "grouped-FFN time vs rows per expert and active experts",
+              "unit": "us", "dtype": "bf16", "data": "synthetic N(0,1) x, N(0,1/fan_in) weights",
+              "shapes": []}
+    for name, d, d_ff, E in shapes:
+        g = torch.Generator(device=dev).manual_seed(0)
+        W = [torch.randn((E, a, b), generator=g, device=dev, dtype=torch.float32).div_(b ** 0.5).to(torch.bfloat16)
+             for a, b in ((d_ff, d), (d_ff, d), (d, d_ff))]
+        pts = []
+        for G in Gs:
+            for n in ns:
+                rows = G * n
+                if rows > 65536:
+                    continue
+                counts = np.zeros(E, np.int64)
+                counts[np.linspace(0, E - 1, G).astype(int)] = n   # spread over the expert range
+                offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+                xs = torch.randn((rows, d), generator=g, device=dev).to(torch.bfloat16)
+                ys = torch.empty((rows, d), device=dev)
+                ws = moe.Workspace(moe.moe_ffn_workspace_size(rows, E, d, d_ff, torch.bfloat16, torch.bfloat16), device=dev)
+                t = _time_calls(lambda: moe.moe_grouped_ffn(xs, offs, W[0], W[1], W[2], ys, ws), max(args.steps // 2, 5))
+                us = float(np.median(t))
+                pts.append((G, n, rows, us))
+                log(f"{name}: G={G} n={n}: {us:.1f} us")
+                del xs, ys, ws
+        # fit: the streaming branch on the small-n points, the row branch on the large-n points
+        P = np.array(pts, dtype=np.float64)
+        small = P[P[:, 1] <= 8]
+        large = P[P[:, 1] >= 1024]
+        A1 = np.stack([np.ones(len(small)), small[:, 0]], 1)
+        a, b = np.linalg.lstsq(A1, small[:, 3], rcond=None)[0]
+        A2 = np.stack([np.ones(len(large)), large[:, 2]], 1)
+        c, beta = np.linalg.lstsq(A2, large[:, 3], rcond=None)[0]
+        model = np.maximum(a + b * P[:, 0], c + beta * P[:, 2])
+        wbytes = 3 * d * d_ff * 2
+        result["shapes"].append({
+            "shape": name, "d": d, "d_ff": d_ff, "E": E,
+            "points": [{"G": int(G), "n": int(n), "us": round(us, 2)} for G, n, _, us in pts],
+            "fit": {"a_us": round(a, 2), "b_us_per_expert": round(b, 3), "c_us": round(c, 2),
+                    "beta_us_per_row": round(beta, 5),
+                    "max_rel_misfit": round(float(np.max(np.abs(model - P[:, 3]) / P[:, 3])), 3)},
+            "n_star_measured": round(b / beta, 1),
+            "per_expert_stream_GBps": round(wbytes / (b * 1e-6) / 1e9, 1),
+            "row_rate_TFLOPs": round(6 * d * d_ff / (beta * 1e-6) / 1e12, 1),
+            "n_star_roofline_bf16": round(2500e12 / 8e12, 1)})
+        del W
+        torch.cuda.empty_cache()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _timed_steps(fn, steps: int, warmup: int) -> float:
+    """ms per call of fn over `steps` calls after `warmup` untimed ones (synchronised)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def capacity_sweep(args, cfg, logits, x, W, out, ws, skw) -> int:
+    """Capacity factor C = 1.0..2.0 (tutorial page, section 10, exercise D): layer tokens/s and
+    the fraction of dropped assignments, next to the uncapped layer."""
+    import torch
+    import token_dispatch_expert_amd as moe
+    T, E, k = cfg.T, cfg.E, cfg.k
+    rows = []
+    for pct in (None, 200, 175, 150, 125, 110, 100):
+        cap = None if pct is None else moe.moe_expert_capacity(T, E, k, pct)
+        ms = _timed_steps(lambda: moe.moe_layer(logits, x, W["gate"], W["up"], W["down"], k, out, ws,
+                                                capacity=cap, **skw), args.steps, args.warmup)
+        kept = int(out["offsets"][-1].item())
+        rows.append({"C": None if pct is None else pct / 100, "capacity": cap, "ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(T / (ms / 1e3), 1), "dropped_frac": round(1 - kept / (T * k), 4),
+                     "active_experts": int(torch.count_nonzero(out["counts"]).item())})
+        log(f"C={rows[-1]['C']}: capacity {cap}, {ms * 1e3:.1f} us/step, dropped {rows[-1]['dropped_frac']:.2%}")
+    print(json.dumps({"metric": "layer tokens/s and dropped fraction vs capacity factor",
+                      "config": {"workload": f"{cfg.name}: {cfg.note}", "T": T, "E": E, "k": k,
+                                 "d": cfg.d, "d_ff": cfg.d_ff, "weights": cfg.w},
+                      "steps": args.steps, "warmup": args.warmup, "sweep": rows}), flush=True)
+    return 0
+
+
+def naive_baselines(args, cfg, logits, x, W, out, ws, skw) -> int:
+    """The tutorial's exercise C (section 10; "sorting matters", section 8): (i) a per-token
+    loop with no sort, every (token, expert) pair its own GEMV chain, and (ii) a per-expert
+    launch loop after a sort, each expert's rows as separate library GEMMs, both in torch on the
+    same GPU, against the grouped path (one moe_layer call). bf16 weights only."""
+    import numpy as np
+    import torch
+    import token_dispatch_expert_amd as moe
+    if cfg.w != "bf16":
+        log("naive baselines are written for bf16 weights")
+        return 2
+    T, E, k = cfg.T, cfg.E, cfg.k
+    Wg, Wu, Wd = W["gate"], W["up"], W["down"]
+
+    def grouped():
+        moe.moe_layer(logits, x, Wg, Wu, Wd, k, out, ws)
+
+    ms_grouped = _timed_steps(grouped, args.steps, args.warmup)
+    y_ref = out["y"].clone()
+    ids = out["topk_ids"].long()
+    gates = out["topk_gates"]
+    ids_h = ids.cpu().numpy()
+
+    def silu_mul(g, u):
+        gf = g.float()
+        return (gf * torch.sigmoid(gf) * u.float()).to(torch.bfloat16)
+
+    def per_token():
+        y = torch.zeros((T, cfg.d), dtype=torch.float32, device=x.device)
+        for t in range(T):
+            xt = x[t:t + 1]
+            for j in range(k):
+                e = int(ids_h[t, j])
+                h = silu_mul(xt @ Wg[e].t(), xt @ Wu[e].t())
+                y[t] += gates[t, j] * (h @ Wd[e].t()).float()[0]
+        return y
+
+    def per_expert():
+        flat = ids.reshape(-1)
+        order = torch.argsort(flat, stable=True)
+        counts = torch.bincount(flat, minlength=E).cpu().tolist()
+        xs = x[order // k]
+        ys = torch.empty((T * k, cfg.d), dtype=torch.float32, device=x.device)
+        r = 0
+        for e, n in enumerate(counts):
+            if n:
+                xe = xs[r:r + n]
+                h = silu_mul(xe @ Wg[e].t(), xe @ Wu[e].t())
+                ys[r:r + n] = (h @ Wd[e].t()).float()
+                r += n
+        y = torch.zeros((T, cfg.d), dtype=torch.float32, device=x.device)
+        y.index_add_(0, order // k, ys * gates.reshape(-1)[order, None])
+        return y
+
+    n_tok = 1 if T > 1024 else max(1, args.steps // 4)
+    ms_tok = _timed_steps(per_token, n_tok, 1)
+    ms_exp = _timed_steps(per_expert, args.steps, args.warmup)
+    def rel(a):
+        a, b = a.double(), y_ref.double()
+        return float((a - b).abs().max() / b.pow(2).mean().sqrt())
+    err_tok, err_exp = rel(per_token()), rel(per_expert())
+    res = {"metric": "layer time: grouped path vs naive per-token and per-expert loops",
+           "config": {"workload": f"{cfg.name}: {cfg.note}", "T": T, "E": E, "k": k, "d": cfg.d,
+                      "d_ff": cfg.d_ff},
+           "grouped_ms": round(ms_grouped, 4),
+           "per_token_loop_ms": round(ms_tok, 2), "per_expert_loop_ms": round(ms_exp, 4),
+           "speedup_vs_per_token": round(ms_tok / ms_grouped, 1),
+           "speedup_vs_per_expert": round(ms_exp / ms_grouped, 2),
+           "rel_err_vs_grouped": {"per_token": round(err_tok, 4), "per_expert": round(err_exp, 4)},
+           "per_token_steps_timed": n_tok}
+    log(json.dumps(res))
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +267,12 @@ def main() -> int:
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--capacity-sweep", action="store_true",
+                    help="layer tokens/s and drop rate for capacity factors 1.0..2.0")
+    ap.add_argument("--expert-time-sweep", action="store_true",
+                    help="grouped-FFN time over rows per expert and active experts (max-affine fit)")
+    ap.add_argument("--naive-baselines", action="store_true",
+                    help="per-token and per-expert torch loops against the grouped path")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -97,6 +294,8 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy(max(args.steps, 1))
         return 0
+    if args.expert_time_sweep:
+        return expert_time_sweep(args)
 
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.config]
@@ -140,6 +339,11 @@ def main() -> int:
 
     def step():
         moe.moe_layer(logits, x, W["gate"], W["up"], W["down"], k, out, ws, **skw)
+
+    if args.capacity_sweep:
+        return capacity_sweep(args, cfg, logits, x, W, out, ws, skw)
+    if args.naive_baselines:
+        return naive_baselines(args, cfg, logits, x, W, out, ws, skw)
 
     # ---- warmup, then exactly K timed steps bracketed by synchronisation
     for _ in range(args.warmup):

@@ -30,6 +30,11 @@ oracle takes the readings listed below (each is also listed in the design notes)
   R7 (optional, off by default) h_round="bf16": h is rounded to the nearest bf16 between the
      two GEMMs, the rounding point of a bf16 implementation; tests use it as a second,
      tighter comparison next to the plain fp64 one.
+  R9 router scores (the fused router's input side; same page, section 4: the router decides
+     each token's experts): logits[t, e] = sum_i x[t, i] * w_router[e, i], one weight row per
+     expert, no bias or scaling; exact decode, fp64. The top-k of the fused GPU router is
+     checked by routing the GPU's own fp32 logits with `route` (a selection decided in floating
+     point is compared in the precision that decided it), and those logits against these.
   R8 capacity factor (optional; same page, section 5, mitigation 1, and section 10, exercise
      D): each expert keeps at most `capacity` assignments and the excess is dropped. The page
      states capacity = C * tokens / E; with k > 1 the count is of assignments, so
@@ -119,6 +124,13 @@ def route(logits: np.ndarray, k: int):
         ids[t] = chosen
         gates[t] = w / np.sum(w)
     return ids, gates
+
+
+def router_logits(x: np.ndarray, x_fmt: str, w_router: np.ndarray, w_fmt: str) -> np.ndarray:
+    """Router scores [T, E] = X W_r^T in fp64 from the exactly decoded stored values (R9)."""
+    X = decode_activations(x, x_fmt)
+    Wr = decode_matrix(w_router, w_fmt)
+    return X @ Wr.T
 
 
 # ----------------------------------------------------------------------------------------

@@ -339,13 +339,36 @@ def check_capacity_brute_force_layer():
                 assert oracle.rel_max_err(out["y"], ref) < 1e-12, (seed, cap)
 
 
+def check_router_logits():
+    rng = np.random.default_rng(41)
+    # brute force (explicit sums over the contraction) and torch's fp64 matmul on tiny inputs
+    for T, E, d in [(5, 3, 7), (9, 6, 32), (1, 4, 64)]:
+        xb = synth.round_to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+        wb = synth.round_to_bf16((rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32))
+        got = oracle.router_logits(xb, "bf16", wb, "bf16")
+        X, Wr = oracle.decode_bf16(xb), oracle.decode_bf16(wb)
+        want = np.array([[math.fsum(X[t, i] * Wr[e, i] for i in range(d)) for e in range(E)] for t in range(T)])
+        assert got.shape == (T, E)
+        assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+        tw = (torch.from_numpy(X) @ torch.from_numpy(Wr).T).numpy()
+        assert np.allclose(got, tw, rtol=1e-12, atol=1e-14)
+    # one-hot router rows pick single columns of x, exactly
+    T, d, E = 8, 40, 5
+    xb = synth.round_to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+    cols = [3, 0, 39, 17, 3]
+    w = np.zeros((E, d), np.float32)
+    w[np.arange(E), cols] = 1.0
+    got = oracle.router_logits(xb, "bf16", synth.round_to_bf16(w), "bf16")
+    assert np.array_equal(got, oracle.decode_bf16(xb)[:, cols])
+
+
 CHECKS = [
     check_decode_bf16, check_decode_e4m3fn, check_route_vs_stable_argsort,
     check_route_special_cases, check_permute_vs_library, check_golden_load_example,
     check_golden_volume_example, check_swiglu_closed_form, check_brute_force_layer,
     check_identity_experts_and_gather, check_fp8_dequant_blocks, check_bf16_layer_decodes_inputs,
     check_bf16_value_rounding, check_capacity_formula, check_capacity_golden_example,
-    check_capacity_vs_library, check_capacity_brute_force_layer,
+    check_capacity_vs_library, check_capacity_brute_force_layer, check_router_logits,
 ]
 
 
@@ -358,7 +381,7 @@ def test_oracle_pin(check):
 # the pins must catch plausible mistakes planted in the oracle
 # ----------------------------------------------------------------------------------------
 _ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16",
-                                     "expert_capacity")}
+                                     "expert_capacity", "router_logits")}
 
 
 def _mut_route_tie_high(logits, k):
@@ -487,6 +510,18 @@ def _mut_decode_e4m3_bias8(codes):
     return _ORIG["decode_e4m3fn"](codes) / 2.0
 
 
+def _mut_router_drop_last_term(x, x_fmt, w_router, w_fmt):
+    X = om.decode_activations(x, x_fmt)[:, :-1]
+    Wr = om.decode_matrix(w_router, w_fmt)[:, :-1]
+    return X @ Wr.T
+
+
+def _mut_router_untransposed_rows(x, x_fmt, w_router, w_fmt):
+    X = om.decode_activations(x, x_fmt)
+    Wr = om.decode_matrix(w_router, w_fmt)
+    return X @ Wr[::-1].T
+
+
 MUTANTS = {
     "route_tie_high": ("route", _mut_route_tie_high),
     "route_full_softmax": ("route", _mut_route_full_softmax),
@@ -498,6 +533,8 @@ MUTANTS = {
     "permute_cap_plus_one": ("permute", _mut_permute_cap_plus_one),
     "capacity_floor": ("expert_capacity", _mut_capacity_floor),
     "combine_keeps_dropped": ("combine", _mut_combine_keeps_dropped),
+    "router_drop_last_term": ("router_logits", _mut_router_drop_last_term),
+    "router_reversed_experts": ("router_logits", _mut_router_untransposed_rows),
     "ffn_silu_on_up": ("expert_ffn", _mut_ffn_silu_on_up),
     "ffn_sigmoid_only": ("expert_ffn", _mut_ffn_sigmoid_only),
     "ffn_down_untransposed": ("expert_ffn", _mut_ffn_down_untransposed),

@@ -76,6 +76,25 @@ const char* moe_status_string(moe_status_t status);
 moe_status_t moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
                        float* topk_gates, int32_t* counts, void* stream);
 
+/*
+ * moe_route_gemm - the router's scores and the top-k gating in one launch, with no round trip
+ * of the logits through memory (tutorial page, section 4: the router decides each token's
+ * destination experts; section 1: each token goes to k of E experts; the scores are the
+ * token's hidden state times one weight row per expert).
+ *
+ *   x          [T, d] bf16, row-major (the tokens' hidden states).
+ *   w_router   [E, d] bf16, row-major (one row per expert, contraction-contiguous).
+ *   logits     [T, E] fp32 out, or NULL: logits[t, e] = sum_i x[t, i] * w_router[e, i], exact
+ *              products summed in fp32 (the order of that sum is the kernel's own).
+ *   topk_ids, topk_gates, counts: as moe_route, computed from these fp32 logits (the same
+ *              selection and gates moe_route gives on them).
+ *   Requires x_dtype = w_dtype = MOE_BF16, E <= 256 and d a multiple of 32
+ *   (MOE_ERR_UNSUPPORTED otherwise).
+ */
+moe_status_t moe_route_gemm(const void* x, moe_dtype_t x_dtype, const void* w_router,
+                            moe_dtype_t w_dtype, int T, int E, int k, int d, float* logits,
+                            int32_t* topk_ids, float* topk_gates, int32_t* counts, void* stream);
+
 /* Bytes of workspace moe_permute needs (0 is possible; then workspace may be NULL). */
 size_t moe_permute_workspace_size(int T, int E, int k);
 

@@ -158,3 +158,23 @@ def test_workspace_sizes(lib):
     assert lib.moe_permute_workspace_size(5, 4, 9) == 0           # invalid -> 0
     assert lib.moe_ffn_workspace_size(65536, 256, 7168, 2048, B.MOE_BF16, B.MOE_FP8_E4M3FN) == 65536 * 2048 * 2
     assert lib.moe_ffn_workspace_size(128, 8, 128, 256, B.MOE_F32, B.MOE_F32) == 128 * 256 * 4
+
+
+def test_route_gemm_rejects_bad_arguments(lib):
+    f = lib.moe_route_gemm
+    ok = [P, B.MOE_BF16, P2, B.MOE_BF16, 16, 8, 2, 64, None, P3, P, None, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x", "xdt", "w", "wdt", "T", "E", "k", "d", "logits", "ids", "gates", "counts", "s"]
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(xdt=B.MOE_F32) == B.MOE_ERR_UNSUPPORTED
+    assert call(wdt=B.MOE_FP8_E4M3FN) == B.MOE_ERR_UNSUPPORTED
+    assert call(E=300) == B.MOE_ERR_UNSUPPORTED            # more experts than one tile row holds
+    assert call(d=48) == B.MOE_ERR_UNSUPPORTED             # not a multiple of 32
+    assert call(k=9) == B.MOE_ERR_INVALID_ARG
+    assert call(x=None) == B.MOE_ERR_INVALID_ARG
+    assert call(logits=MIS) == B.MOE_ERR_INVALID_ARG

@@ -27,6 +27,7 @@ ENTRY_POINTS = (
     "moe_status_string", "moe_route", "moe_permute_workspace_size", "moe_permute",
     "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
     "moe_layer", "moe_expert_capacity", "moe_permute_capped", "moe_layer_capped",
+    "moe_route_gemm",
 )
 
 _lib = None
@@ -64,6 +65,7 @@ def load_library(path: str | None = None):
         "moe_layer": ([P, P, I, I, I, I, I, I, P, P, P, I, P, P, P,
                        P, P, P, P, P, P, P, P, P, P, S, P], I),
         "moe_expert_capacity": ([I, I, I, I], I),
+        "moe_route_gemm": ([P, I, P, I, I, I, I, I, P, P, P, P, P], I),
         "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
                               P, P, P, P, P, P, P, P, P, P, S, P], I),
@@ -156,6 +158,23 @@ def moe_route(logits, k: int, topk_ids, topk_gates, counts=None, stream=None):
         _need(counts, torch.int32, (E,), "counts")
     _check(load_library().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_gates),
                                     _ptr(counts), _stream(stream)))
+
+
+def moe_route_gemm(x, w_router, k: int, topk_ids, topk_gates, counts=None, logits=None,
+                   stream=None):
+    """Router scores x @ w_router^T (fp32) and top-k gating in one launch; logits optional."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    _need(w_router, x.dtype, (E, d), "w_router")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(topk_gates, torch.float32, (T, k), "topk_gates")
+    if counts is not None:
+        _need(counts, torch.int32, (E,), "counts")
+    if logits is not None:
+        _need(logits, torch.float32, (T, E), "logits")
+    _check(load_library().moe_route_gemm(
+        _ptr(x), _dt(x, "x"), _ptr(w_router), _dt(w_router, "w_router"), T, E, k, d,
+        _ptr(logits), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _stream(stream)))
 
 
 def moe_permute(x, topk_ids, E: int, counts, offsets, sorted_to_flat, flat_to_sorted, x_sorted,

@@ -154,6 +154,23 @@ moe_status_t moe_route(const float* logits, int T, int E, int k, int32_t* topk_i
                                       static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_route_gemm(const void* x, moe_dtype_t x_dtype, const void* w_router,
+                            moe_dtype_t w_dtype, int T, int E, int k, int d, float* logits,
+                            int32_t* topk_ids, float* topk_gates, int32_t* counts, void* stream) {
+  moe_status_t s = check_sizes(T, E, k);
+  if (s != MOE_OK) return s;
+  if (d < 1 || d > kMaxDim) return MOE_ERR_INVALID_ARG;
+  if (x_dtype != MOE_BF16 || w_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > moe::kRouterMaxExperts || d % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long R = (long long)T * k;
+  if (!ok_ptr(x, (long long)T * d, 16) || !ok_ptr(w_router, (long long)E * d, 16) ||
+      !ok_ptr(topk_ids, R, 4) || !ok_ptr(topk_gates, R, 4))
+    return MOE_ERR_INVALID_ARG;
+  if ((logits && !aligned(logits, 4)) || (counts && !aligned(counts, 4))) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route_gemm(x, w_router, T, E, k, d, logits, topk_ids, topk_gates,
+                                           counts, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_permute_workspace_size(int T, int E, int k) {
   if (check_sizes(T, E, k) != MOE_OK) return 0;
   return align_up(moe::permute_workspace_ints(T, E, k) * sizeof(int32_t), 256);

@@ -44,6 +44,13 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t value, hipStream_t stream)
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
                         int32_t* counts, hipStream_t stream);
 
+// fused router GEMM + top-k: bf16 x [T, d] and w_router [E, d], E <= kRouterMaxExperts,
+// d a multiple of 32; logits (nullable) receives the fp32 logits [T, E]
+constexpr int kRouterMaxExperts = 256;
+hipError_t launch_route_gemm(const void* x, const void* w_router, int T, int E, int k, int d,
+                             float* logits, int32_t* ids, float* gates, int32_t* counts,
+                             hipStream_t stream);
+
 // workspace: n_tiles * E int32 (per-tile histograms, then per-tile bases)
 size_t permute_workspace_ints(int T, int E, int k);
 // cap: most kept assignments per expert (INT_MAX: no capacity limit)

@@ -161,6 +161,39 @@ def _timed_steps(fn, steps: int, warmup: int) -> float:
     return (time.perf_counter() - t0) / steps * 1e3
 
 
+def router_bench(args) -> int:
+    """moe_route_gemm (router scores + top-k in one launch, logits not written) at the c2 and c4
+    router shapes: time per call with cold caches, against HBM (x once, router weights once, ids
+    and gates) and against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+    import token_dispatch_expert_amd as moe
+    dev = torch.device("cuda:0")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    res = []
+    for name, T, d, E, k in (("c2", 128, 4096, 128, 8), ("c4", 8192, 7168, 256, 8)):
+        g = torch.Generator(device=dev).manual_seed(1)
+        x = torch.randn((T, d), generator=g, device=dev).to(torch.bfloat16)
+        w = torch.randn((E, d), generator=g, device=dev).div_(d ** 0.5).to(torch.bfloat16)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        samples = []
+        for _ in range(max(args.steps, 5)):
+            flush.sum()
+            torch.cuda.synchronize()
+            samples += _time_calls(lambda: moe.moe_route_gemm(x, w, k, ids, gates), 1, 0)
+        us = float(np.median(samples))
+        byts = T * d * 2 + E * d * 2 + T * k * 8
+        flops = 2.0 * T * E * d
+        res.append({"shape": name, "T": T, "d": d, "E": E, "k": k, "median_us": round(us, 2),
+                    "GB_per_s": round(byts / (us * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 2)})
+        log(f"router {name}: {us:.1f} us")
+    print(json.dumps({"metric": "fused router GEMM + top-k time", "unit": "us", "results": res}), flush=True)
+    return 0
+
+
 def capacity_sweep(args, cfg, logits, x, W, out, ws, skw) -> int:
     """Capacity factor C = 1.0..2.0 (tutorial page, section 10, exercise D): layer tokens/s and
     the fraction of dropped assignments, next to the uncapped layer."""
@@ -273,6 +306,8 @@ def main() -> int:
                     help="grouped-FFN time over rows per expert and active experts (max-affine fit)")
     ap.add_argument("--naive-baselines", action="store_true",
                     help="per-token and per-expert torch loops against the grouped path")
+    ap.add_argument("--router", action="store_true",
+                    help="time the fused router GEMM + top-k at the decode and prefill shapes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -296,6 +331,8 @@ def main() -> int:
         return 0
     if args.expert_time_sweep:
         return expert_time_sweep(args)
+    if args.router:
+        return router_bench(args)
 
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.config]

@@ -88,12 +88,19 @@ moe_status_t moe_route(const float* logits, int T, int E, int k, int32_t* topk_i
  *              products summed in fp32 (the order of that sum is the kernel's own).
  *   topk_ids, topk_gates, counts: as moe_route, computed from these fp32 logits (the same
  *              selection and gates moe_route gives on them).
+ *   workspace  >= moe_route_gemm_workspace_size(T, E, k) bytes, 16-byte aligned (batches of
+ *              up to 1024 tokens split the contraction over several workgroups and keep fp32
+ *              partial scores there; larger batches need none and may pass NULL).
  *   Requires x_dtype = w_dtype = MOE_BF16, E <= 256 and d a multiple of 32
  *   (MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status_t moe_route_gemm(const void* x, moe_dtype_t x_dtype, const void* w_router,
                             moe_dtype_t w_dtype, int T, int E, int k, int d, float* logits,
-                            int32_t* topk_ids, float* topk_gates, int32_t* counts, void* stream);
+                            int32_t* topk_ids, float* topk_gates, int32_t* counts,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace moe_route_gemm needs (0 for invalid sizes or large batches). */
+size_t moe_route_gemm_workspace_size(int T, int E, int k);
 
 /* Bytes of workspace moe_permute needs (0 is possible; then workspace may be NULL). */
 size_t moe_permute_workspace_size(int T, int E, int k);

@@ -162,11 +162,14 @@ def test_workspace_sizes(lib):
 
 def test_route_gemm_rejects_bad_arguments(lib):
     f = lib.moe_route_gemm
-    ok = [P, B.MOE_BF16, P2, B.MOE_BF16, 16, 8, 2, 64, None, P3, P, None, None]
+    wsb = lib.moe_route_gemm_workspace_size(16, 8, 2)
+    assert wsb == 16 * 16 * 8 * 4                          # 16 contraction chunks of fp32 partials
+    assert lib.moe_route_gemm_workspace_size(4096, 8, 2) == 0
+    ok = [P, B.MOE_BF16, P2, B.MOE_BF16, 16, 8, 2, 64, None, P3, P, None, P2, wsb, None]
 
     def call(**kw):
         a = list(ok)
-        names = ["x", "xdt", "w", "wdt", "T", "E", "k", "d", "logits", "ids", "gates", "counts", "s"]
+        names = ["x", "xdt", "w", "wdt", "T", "E", "k", "d", "logits", "ids", "gates", "counts", "ws", "wsb", "s"]
         for n, v in kw.items():
             a[names.index(n)] = v
         return f(*a)
@@ -178,3 +181,5 @@ def test_route_gemm_rejects_bad_arguments(lib):
     assert call(k=9) == B.MOE_ERR_INVALID_ARG
     assert call(x=None) == B.MOE_ERR_INVALID_ARG
     assert call(logits=MIS) == B.MOE_ERR_INVALID_ARG
+    assert call(ws=None) == B.MOE_ERR_WORKSPACE
+    assert call(wsb=wsb - 4) == B.MOE_ERR_WORKSPACE

@@ -34,18 +34,20 @@ def run(dev, x, w, k, with_logits=True):
     E = w.shape[0]
     xd, wd = H.to_dev(x, "bf16", dev), H.to_dev(w, "bf16", dev)
     ids = torch.full((T, k), -5, dtype=torch.int32, device=dev)
+    ws = moe.Workspace(moe.moe_route_gemm_workspace_size(T, E, k), device=dev)
     gates = torch.full((T, k), float("nan"), device=dev)
     counts = torch.full((E,), -5, dtype=torch.int32, device=dev)
     lg = torch.full((T, E), float("nan"), device=dev) if with_logits else None
-    moe.moe_route_gemm(xd, wd, k, ids, gates, counts, lg)
+    moe.moe_route_gemm(xd, wd, k, ids, gates, counts, lg, workspace=ws)
     torch.cuda.synchronize()
     return (ids.cpu().numpy(), gates.cpu().numpy(), counts.cpu().numpy(),
             None if lg is None else lg.cpu().numpy())
 
 
 @pytest.mark.parametrize("T,E,k,d,dup", [
-    (128, 128, 8, 4096, None),        # decode-shape router
-    (8192, 256, 8, 7168, None),       # prefill DeepSeek-V3-shaped router
+    (128, 128, 8, 4096, None),        # decode-shape router (contraction split over workgroups)
+    (2000, 96, 4, 256, None),         # one fused pass, 16-token tiles
+    (8192, 256, 8, 7168, None),       # prefill DeepSeek-V3-shaped router (32-token tiles)
     (37, 40, 5, 96, None),            # ragged token tile, E not a multiple of 16
     (1, 8, 8, 32, None),              # k = E, one token
     (300, 64, 6, 128, [(5, 9), (9, 12), (0, 63)]),  # exact ties between experts

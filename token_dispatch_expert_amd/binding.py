@@ -27,7 +27,7 @@ ENTRY_POINTS = (
     "moe_status_string", "moe_route", "moe_permute_workspace_size", "moe_permute",
     "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
     "moe_layer", "moe_expert_capacity", "moe_permute_capped", "moe_layer_capped",
-    "moe_route_gemm",
+    "moe_route_gemm", "moe_route_gemm_workspace_size",
 )
 
 _lib = None
@@ -65,7 +65,8 @@ def load_library(path: str | None = None):
         "moe_layer": ([P, P, I, I, I, I, I, I, P, P, P, I, P, P, P,
                        P, P, P, P, P, P, P, P, P, P, S, P], I),
         "moe_expert_capacity": ([I, I, I, I], I),
-        "moe_route_gemm": ([P, I, P, I, I, I, I, I, P, P, P, P, P], I),
+        "moe_route_gemm": ([P, I, P, I, I, I, I, I, P, P, P, P, P, S, P], I),
+        "moe_route_gemm_workspace_size": ([I, I, I], S),
         "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
                               P, P, P, P, P, P, P, P, P, P, S, P], I),
@@ -160,11 +161,18 @@ def moe_route(logits, k: int, topk_ids, topk_gates, counts=None, stream=None):
                                     _ptr(counts), _stream(stream)))
 
 
+def moe_route_gemm_workspace_size(T: int, E: int, k: int) -> int:
+    return load_library().moe_route_gemm_workspace_size(T, E, k)
+
+
 def moe_route_gemm(x, w_router, k: int, topk_ids, topk_gates, counts=None, logits=None,
-                   stream=None):
-    """Router scores x @ w_router^T (fp32) and top-k gating in one launch; logits optional."""
+                   workspace: "Workspace | None" = None, stream=None):
+    """Router scores x @ w_router^T (fp32) and top-k gating; logits optional. Small batches
+    need a workspace of moe_route_gemm_workspace_size bytes (allocated here if not given)."""
     T, d = x.shape
     E = w_router.shape[0]
+    if workspace is None:
+        workspace = Workspace(moe_route_gemm_workspace_size(T, E, k), device=x.device)
     _need(w_router, x.dtype, (E, d), "w_router")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(topk_gates, torch.float32, (T, k), "topk_gates")
@@ -174,7 +182,8 @@ def moe_route_gemm(x, w_router, k: int, topk_ids, topk_gates, counts=None, logit
         _need(logits, torch.float32, (T, E), "logits")
     _check(load_library().moe_route_gemm(
         _ptr(x), _dt(x, "x"), _ptr(w_router), _dt(w_router, "w_router"), T, E, k, d,
-        _ptr(logits), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), _stream(stream)))
+        _ptr(logits), _ptr(topk_ids), _ptr(topk_gates), _ptr(counts), workspace.ptr,
+        workspace.nbytes, _stream(stream)))
 
 
 def moe_permute(x, topk_ids, E: int, counts, offsets, sorted_to_flat, flat_to_sorted, x_sorted,

@@ -154,9 +154,15 @@ moe_status_t moe_route(const float* logits, int T, int E, int k, int32_t* topk_i
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_route_gemm_workspace_size(int T, int E, int k) {
+  if (check_sizes(T, E, k) != MOE_OK || E > moe::kRouterMaxExperts) return 0;
+  return moe::route_gemm_workspace_bytes(T, E);
+}
+
 moe_status_t moe_route_gemm(const void* x, moe_dtype_t x_dtype, const void* w_router,
                             moe_dtype_t w_dtype, int T, int E, int k, int d, float* logits,
-                            int32_t* topk_ids, float* topk_gates, int32_t* counts, void* stream) {
+                            int32_t* topk_ids, float* topk_gates, int32_t* counts,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   moe_status_t s = check_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (d < 1 || d > kMaxDim) return MOE_ERR_INVALID_ARG;
@@ -167,8 +173,11 @@ moe_status_t moe_route_gemm(const void* x, moe_dtype_t x_dtype, const void* w_ro
       !ok_ptr(topk_ids, R, 4) || !ok_ptr(topk_gates, R, 4))
     return MOE_ERR_INVALID_ARG;
   if ((logits && !aligned(logits, 4)) || (counts && !aligned(counts, 4))) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::route_gemm_workspace_bytes(T, E);
+  if (need > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
+    return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_route_gemm(x, w_router, T, E, k, d, logits, topk_ids, topk_gates,
-                                           counts, static_cast<hipStream_t>(stream)));
+                                           counts, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_permute_workspace_size(int T, int E, int k) {

@@ -46,10 +46,14 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 
 // fused router GEMM + top-k: bf16 x [T, d] and w_router [E, d], E <= kRouterMaxExperts,
 // d a multiple of 32; logits (nullable) receives the fp32 logits [T, E]
+// Batches of at most kRouterSplitMaxT tokens split the contraction over several workgroups and
+// need route_gemm_workspace_bytes of workspace (fp32 partial logits); larger ones need none.
 constexpr int kRouterMaxExperts = 256;
+constexpr int kRouterSplitMaxT = 1024;
+size_t route_gemm_workspace_bytes(int T, int E);
 hipError_t launch_route_gemm(const void* x, const void* w_router, int T, int E, int k, int d,
                              float* logits, int32_t* ids, float* gates, int32_t* counts,
-                             hipStream_t stream);
+                             void* workspace, hipStream_t stream);
 
 // workspace: n_tiles * E int32 (per-tile histograms, then per-tile bases)
 size_t permute_workspace_ints(int T, int E, int k);

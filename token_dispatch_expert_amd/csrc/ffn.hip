@@ -709,8 +709,9 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 // ffn_tiled_kernel, but operands go from memory straight into LDS (global_load_lds, 16 bytes
 // per lane, no register staging) through a ring of RING contraction steps of DK elements,
 // keeping RING-1 steps of loads in flight while the MFMAs consume the oldest one. Two shapes:
-//  - prefill, 256 x 256 tiles, DK = 32, 4 slots: the operands mostly hit in L2 and the ring
-//    covers L2-miss latency at the MFMA rate;
+//  - prefill, 256 x 256 tiles, DK = 64, 2 slots (128 KB): the operands mostly hit in L2, one
+//    barrier per 64-wide step (half as many as with 32-wide steps measured 7% faster), the next
+//    step's loads in flight while the MFMAs consume the current one;
 //  - decode, 64 x 128 tiles, DK = 64, 3 slots, two workgroups per CU: weight streaming, where
 //    each weight row is read a full 128-byte line per step (64-byte pieces of many rows
 //    measured ~15% below line-sized ones in HBM throughput).
@@ -718,6 +719,18 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 // tile (see dswz).
 constexpr int kDK = 32;     // contraction step
 constexpr int kFp8DlMaxK = 65536;  // longest contraction of the fp8 direct-to-LDS kernel
+// Word 3 of a raw buffer descriptor (32-bit data format, bounds-checked offsets): loads at or
+// past num_records bytes return zeros.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from a buffer into LDS at lds + 16 * lane (the loads are wrapped in a device
+// function: called directly from a kernel template, the host compilation pass drops the
+// kernel's launch stub)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset,
+                                                  int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, soffset, 0, 0);
+}
 constexpr int kRing = 4;    // LDS ring depth
 
 // LDS image of a tile row of CPR chunks of 16 bytes: chunk c of row r sits at chunk c ^ x(r),
@@ -816,8 +829,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
     const int nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
     const int c0 = nt * cols_per_tile;
     // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
-    // issued: those LDS rows keep stale data, which only reaches accumulator rows that are
-    // never stored (row r of the product depends on row r of A alone).
+    // issued, and the 16-row fragments past it take no LDS reads and no MFMAs: those LDS rows
+    // keep stale data, which could only reach accumulator rows that are never stored (row r of
+    // the product depends on row r of A alone).
     constexpr int RPI = 64 / CPRA;  // tile rows per A load instruction
     int aiw = 0;
 #pragma unroll
@@ -825,48 +839,56 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
       aiw += (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows)) ? 1 : 0;
     const int lpw = aiw + BIW;  // this wave's loads per step
 
-    // per-lane source of each of this wave's load instructions (byte offsets at step 0)
-    size_t a_src[AIW], b_src[BIW];
-    bool b_up[BIW];
-#pragma unroll
-    for (int i = 0; i < AIW; ++i) {
-      const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the A tile
+    // Loads are buffer loads into LDS: a descriptor per operand holds the tile's base and its
+    // byte extent (rows past the expert's last row, or past the last column, read as zeros, so
+    // nothing is clamped), one 32-bit lane offset serves all of a wave's load instructions, and
+    // the per-instruction and per-step parts are wave-uniform scalar offsets. That keeps the
+    // address registers at two, whatever the number of load instructions.
+    // Instruction i of this wave covers tile rows shifted by i * NW * rows-per-instruction; the
+    // XOR swizzle of a row repeats with that period, so the lane's chunk is the same for all i.
+    const uint8_t* Xt = static_cast<const uint8_t*>(p.X) + (size_t)r0 * p.K * 2;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)Xt, (short)0, (int)((unsigned)nrows * (unsigned)p.K * 2u), kBufferWord3);
+    const size_t wcol = (size_t)c0 * p.K * WB;  // the tile's first B row (weight row c0)
+    const size_t bbytes = (size_t)(p.N - c0) * p.K * WB;
+    const unsigned bext = bbytes > 0xffffffffu ? 0xffffffffu : (unsigned)bbytes;
+    const __amdgpu_buffer_rsrc_t rB1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const uint8_t*>(p.W1) + (size_t)e * wstride + wcol), (short)0, (int)bext, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rB2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const uint8_t*>(p.W2) + (size_t)e * wstride + wcol), (short)0, (int)bext, kBufferWord3) : rB1;
+    constexpr int RPA = 64 / CPRA, RPB = 64 / CPRB;  // tile rows per load instruction
+    int a_lane, b_lane;  // byte offsets of instruction 0 (this lane)
+    {
+      const int q = wave * 64 + lane;
       const int r = q / CPRA, c = dswz<CPRA>(r, q % CPRA) - r * CPRA;  // source chunk (XOR involution)
-      a_src[i] = ((size_t)(r0 + min(r, nrows - 1)) * p.K) * 2 + c * 16;
+      a_lane = (r * p.K * 2) + c * 16;
     }
-#pragma unroll
-    for (int i = 0; i < BIW; ++i) {
-      const int q = (wave + i * NW) * 64 + lane;          // chunk slot in the B tile
+    // B row t of the tile -> weight row offset from c0 (gated tiles interleave gate and up
+    // halves of WN rows per wave block)
+    auto b_row = [&](int t) __attribute__((always_inline)) {
+      return GATED ? (t / WN) * (WN / 2) + (t % WN) % (WN / 2) : t;
+    };
+    {
+      const int q = wave * 64 + lane;
       const int t = q / CPRB, c = dswz<CPRB>(t, q % CPRB) - t * CPRB;
-      int n;
-      if constexpr (GATED) {
-        const int blk = t / WN, qq = t % WN;
-        b_up[i] = qq >= WN / 2;
-        n = c0 + blk * (WN / 2) + (qq % (WN / 2));
-      } else {
-        b_up[i] = false;
-        n = c0 + t;
-      }
-      b_src[i] = (size_t)e * wstride + (size_t)min(n, p.N - 1) * p.K * WB + c * 16;
+      b_lane = b_row(t) * p.K * WB + c * 16;
     }
-    const uint8_t* X = static_cast<const uint8_t*>(p.X);
-    const uint8_t* W1 = static_cast<const uint8_t*>(p.W1);
-    const uint8_t* W2 = GATED ? static_cast<const uint8_t*>(p.W2) : W1;
+    const int t0w = wave * RPB;  // first B row of this wave's instruction 0 (wave-uniform)
 
     auto issue = [&](int st) __attribute__((always_inline)) {
       u32x4* slot = ring + (st % RING) * STAGE;
-      const size_t ka = (size_t)st * DK * 2, kb = (size_t)st * DK * WB;
+      const int ka = st * DK * 2, kb = st * DK * WB;
 #pragma unroll
       for (int i = 0; i < AIW; ++i)
-        if (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows))
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(X + a_src[i] + ka),
-              (__attribute__((address_space(3))) void*)(slot + (wave + i * NW) * 64), 16, 0, 0);
+        if (loads_a && (!ASKIP || (wave + i * NW) * RPA < nrows))
+          buffer_load_lds16(rA, slot + (wave + i * NW) * 64, a_lane, i * NW * RPA * p.K * 2 + ka);
 #pragma unroll
-      for (int i = 0; i < BIW; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)((b_up[i] ? W2 : W1) + b_src[i] + kb),
-            (__attribute__((address_space(3))) void*)(slot + ACH + (wave + i * NW) * 64), 16, 0, 0);
+      for (int i = 0; i < BIW; ++i) {
+        const int ti = t0w + i * NW * RPB;  // first row of instruction i (wave-uniform)
+        const bool up = GATED && (ti % WN) >= WN / 2;
+        buffer_load_lds16(up ? rB2 : rB1, slot + ACH + (wave + i * NW) * 64, b_lane,
+                          (b_row(ti) - b_row(t0w)) * p.K * WB + kb);
+      }
     };
 
     f32x4 acc[MF][NF];
@@ -926,21 +948,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
         }
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) {
+          if (ASKIP && wm * WM + mf * 16 >= nrows) continue;  // wave-uniform: absent rows
           const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
           __builtin_memcpy(&afr[mf], &v, 16);
         }
         // the next loads go out after this slice's fragment reads: DMA writes landing in LDS
         // while the reads are in progress slow both down
         if (h == 0 && st + RING - 1 < nst) issue(st + RING - 1);
+        // one slice's fragments live at a time: the compiler may not hoist the next slice's
+        // reads above these MFMAs (that would need registers the big tile does not have)
+        if (DK / 32 > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
+            if (ASKIP && wm * WM + mf * 16 >= nrows) continue;  // no MFMA work on absent rows
             if constexpr (F8)
               part[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], part[mf][nf], 0, 0, 0);
             else
               acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
           }
+        if (DK / 32 > 1) __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (F8) {
         if ((st + 1) % KBS == 0) {  // end of a 128-long scale block
@@ -1043,10 +1071,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.wdt == MOE_BF16) {
     if (stream_pass) st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<kBF16, true, 128, 64, 2, 4>(tgu, dev, stream) : launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
+      st = big ? launch_tiled_dl<kBF16, true, 128, 64, 2, 4, 2, 64>(tgu, dev, stream) : launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
     if (st == hipSuccess && stream_pass) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
     if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<kBF16, false, 128, 64, 2, 4>(tdn, dev, stream) : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
+      st = big ? launch_tiled_dl<kBF16, false, 128, 64, 2, 4, 2, 64>(tdn, dev, stream) : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);

@@ -705,16 +705,19 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 }
 
 // ---------------------------------------------------------------------------------------
-// Tiled kernel with direct-to-LDS operand loads (bf16 weights). Same tile decomposition as
-// ffn_tiled_kernel, but operands go from memory straight into LDS (global_load_lds, 16 bytes
-// per lane, no register staging) through a ring of RING contraction steps of DK elements,
-// keeping RING-1 steps of loads in flight while the MFMAs consume the oldest one. Two shapes:
+// Tiled kernel with direct-to-LDS operand loads (bf16 or fp8 weights). Same tile decomposition
+// as ffn_tiled_kernel, but operands go from memory straight into LDS (buffer loads into LDS, 16
+// bytes per lane, no register staging) through a ring of RING contraction steps of DK
+// elements, keeping RING-1 steps of loads in flight while the MFMAs consume the oldest one.
+// Shapes:
 //  - prefill, 256 x 256 tiles, DK = 64, 2 slots (128 KB): the operands mostly hit in L2, one
 //    barrier per 64-wide step (half as many as with 32-wide steps measured 7% faster), the next
 //    step's loads in flight while the MFMAs consume the current one;
 //  - decode, 64 x 128 tiles, DK = 64, 3 slots, two workgroups per CU: weight streaming, where
 //    each weight row is read a full 128-byte line per step (64-byte pieces of many rows
-//    measured ~15% below line-sized ones in HBM throughput).
+//    measured ~15% below line-sized ones in HBM throughput);
+//  - prefill fp8: 128 x 256 tiles, DK = 128 (one step per scale block), 2 slots of 64 KB
+//    (8.5% faster than 64-wide steps in 4 slots).
 // The loading lanes pick their source addresses so that the linear LDS image is the swizzled
 // tile (see dswz).
 constexpr int kDK = 32;     // contraction step
@@ -734,13 +737,14 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
 constexpr int kRing = 4;    // LDS ring depth
 
 // LDS image of a tile row of CPR chunks of 16 bytes: chunk c of row r sits at chunk c ^ x(r),
-// x(r) = (r >> 2) & 3 for 4 chunks and (r >> 1) & 7 for 8 chunks, so that the 16 rows read by
-// one fragment load (same chunk) fall on distinct banks.
+// x(r) = (r >> 2) & 3 for 4 chunks, (r >> 1) & 7 for 8 and r & 15 for 16, so that the 16 rows
+// read by one fragment load (same chunk) fall on distinct banks.
 template <int CPR>
 __device__ __forceinline__ int dswz(int row, int chunk) {
-  static_assert(CPR == 4 || CPR == 8, "row width");
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row width");
   if constexpr (CPR == 4) return row * 4 + (chunk ^ ((row >> 2) & 3));
-  else return row * 8 + (chunk ^ ((row >> 1) & 7));
+  else if constexpr (CPR == 8) return row * 8 + (chunk ^ ((row >> 1) & 7));
+  else return row * 16 + (chunk ^ (row & 15));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
@@ -768,8 +772,8 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
-  static_assert(DK == 32 || DK == 64, "contraction step");
-  static_assert(WF == kBF16 || (WF == kFP8 && DK == 64), "weight format");
+  static_assert(DK == 32 || DK == 64 || DK == 128, "contraction step");
+  static_assert(WF == kBF16 || (WF == kFP8 && DK >= 64), "weight format");
   constexpr bool F8 = WF == kFP8;
   constexpr int WB = F8 ? 1 : 2;                        // weight bytes per element
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
@@ -1079,12 +1083,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   }
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl ? launch_tiled_dl<kFP8, true, 64, 64, 2, 4, 4, 64>(tgu, dev, stream)
+    st = fp8_dl ? launch_tiled_dl<kFP8, true, 64, 64, 2, 4, 2, 128>(tgu, dev, stream)
                 : (big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
                        : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream));
   if (st == hipSuccess) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl ? launch_tiled_dl<kFP8, false, 64, 64, 2, 4, 4, 64>(tdn, dev, stream)
+    st = fp8_dl ? launch_tiled_dl<kFP8, false, 64, 64, 2, 4, 2, 128>(tdn, dev, stream)
                 : (big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
                        : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream));
   return st;

@@ -129,16 +129,15 @@ __device__ __forceinline__ void expert_rows(const int32_t* offsets, int e, int r
 
 // Build the item prefix over experts in LDS: pre[e] = first item of expert e; pre[E] = total.
 // offs (optional) receives the clamped row offsets of every expert, offs[0..E].
-// Item of this workgroup in the round of a persistent grid that starts at item `base`, or -1.
+// Item of workgroup b (of G) in the round of a persistent grid that starts at item `base`, or
+// -1.
 // The hardware deals workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), and
 // each XCD has its own L2. To let the workgroups of one XCD share operands, a round's n items
 // are cut into 8 runs of ceil(n / 8) consecutive items and run x goes to the workgroups of XCD
 // x; a short last round is thus spread over all XCDs. Grids that are not a multiple of 8 take
 // items in plain order.
-__device__ __forceinline__ int xcd_round_item(int base, int total) {
+__device__ __forceinline__ int xcd_round_item(int base, int total, int b, int G) {
   constexpr int kXcd = 8;
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
   if (G % kXcd != 0) return base + b < total ? base + b : -1;
   const int n = min(G, total - base);
   const int run = (n + kXcd - 1) / kXcd;
@@ -506,7 +505,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_kernel(TiledArgs p) 
   const int kl = (lane >> 4) * 8;
 
   for (int base = 0; base < total; base += gridDim.x) {
-    const int item = xcd_round_item(base, total);
+    const int item = xcd_round_item(base, total, blockIdx.x, gridDim.x);
     if (item < 0) continue;  // uniform per workgroup
     int lo = 0, hi = p.E;
     while (lo < hi) {
@@ -769,9 +768,12 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // 128-long contraction block accumulate into a partial tile that is then added to the
 // accumulator times the block's scale (identical dequantisation: the scale multiplies the
 // exact fp8 products' fp32 sum, never a rounded weight). fp8 needs DK = 64.
+// The tile loop of one workgroup, which is rank `rank` of `nranks` workgroups sharing the
+// tiles of the experts with more than min_rows and at most max_rows rows.
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false>
-__global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
+__device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem, int rank,
+                                         int nranks, int min_rows, int max_rows) {
   static_assert(DK == 32 || DK == 64 || DK == 128, "contraction step");
   static_assert(WF == kBF16 || (WF == kFP8 && DK >= 64), "weight format");
   constexpr bool F8 = WF == kFP8;
@@ -788,7 +790,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
   constexpr int ACH = TM * CPRA;                        // A chunks per ring slot
   constexpr int STAGE = ACH + TN * CPRB;                // 16-byte chunks per ring slot
   constexpr int KBS = 128 / DK;                         // steps per fp8 scale block
-  extern __shared__ __align__(16) unsigned char smem[];
   const int Epad = (p.E + 1 + 3) & ~3;
   int32_t* pre = reinterpret_cast<int32_t*>(smem);
   int32_t* offs = pre + Epad;
@@ -805,14 +806,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
   const int wm = wave % WGM, wn = wave / WGM;
   constexpr int cols_per_tile = GATED ? TN / 2 : TN;
   const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
-  build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, 0x7fffffff, NT, offs, p.min_rows, TM);
+  build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, max_rows, NT, offs, min_rows, TM);
   const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
   const int nst = p.K / DK;  // K is a multiple of 64 (of 128 for fp8) on this path
   const size_t wstride = (size_t)p.N * p.K * WB;  // bytes per expert matrix
   const int NB = p.N / 128, KBn = p.K / 128;     // fp8 scale blocks
 
-  for (int base = 0; base < total; base += gridDim.x) {
-    const int item = xcd_round_item(base, total);
+  for (int base = 0; base < total; base += nranks) {
+    const int item = xcd_round_item(base, total, rank, nranks);
     if (item < 0) continue;  // uniform per workgroup
     int lo = 0, hi = p.E;
     while (lo < hi) {
@@ -1019,6 +1020,99 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs 
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false>
+__global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  dl_tiles<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP>(p, smem, blockIdx.x, gridDim.x, p.min_rows,
+                                                         0x7fffffff);
+}
+
+// LDS bytes of dl_tiles for a tile shape (prefix arrays, ring, fp8 scale rows)
+template <int WF, int WM, int WN, int WGM, int WGN, int RING, int DK>
+static size_t dl_lds_bytes(const TiledArgs& p) {
+  constexpr int NTH = 64 * WGM * WGN;
+  constexpr int WB = WF == kFP8 ? 1 : 2;
+  return ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + ((NTH + 3) & ~3)) * sizeof(int32_t) +
+         (size_t)RING * (WGM * WM * DK * 2 + WGN * WN * DK * WB) +
+         (WF == kFP8 ? (size_t)WGN * 2 * (p.K / 128) * sizeof(float) : 0);
+}
+
+// Prefill grouped GEMM in one launch with two kinds of workgroups. Experts with at most
+// kStreamMaxRows rows only stream their weights (HBM-bound); the others are MFMA-bound tiles
+// that mostly hit in L2. The first X workgroups take the small experts in 16-row tiles (COLD
+// shape) while the other G - X take the large ones (HOT shape), so the weight streaming runs
+// on a few CUs beside the matrix work instead of after it (c4: -8.5%, c5: -11% FFN time against
+// separate streaming and tiled launches). X balances the two: bytes of the small experts'
+// weights at kColdCuGBps per CU against the large experts' tile flops at kHotCuTflops per CU,
+// computed identically by every workgroup from the routed counts. The constants are effective
+// rates picked by sweeping them on MI355X (25/30/35/50 GB/s): 30 was best for both prefill
+// workloads; the split is coarse (multiples of 8 CUs), and too few streaming CUs costs far more
+// than too many.
+constexpr float kColdCuGBps = 30.0f;    // weight streaming per CU, GB/s (effective)
+constexpr float kHotCuTflops = 4.0f;    // tile MFMA rate per CU, TFLOP/s
+template <int WF, bool GATED, int HWM, int HWN, int HRING, int HDK, int CWN, int CRING, int CDK>
+__global__ __launch_bounds__(512) void ffn_prefill_kernel(TiledArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int HTM = 2 * HWM, HTN = 4 * HWN;   // hot tiles: 2 x 4 waves
+  constexpr int WB = WF == kFP8 ? 1 : 2;
+  // work of each kind from the counts (one wave; the others wait at the barrier)
+  __shared__ float work[2];
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    float cold_bytes = 0.f, hot_flops = 0.f;
+    for (int e = lane; e < p.E; e += kWave) {
+      int a, b;
+      expert_rows(p.offsets, e, p.rows, a, b);
+      const int n = b - a;
+      const float wbytes = (GATED ? 2.f : 1.f) * (float)p.N * (float)p.K * WB;
+      if (n > 0 && n <= kStreamMaxRows) cold_bytes += wbytes;
+      else if (n > kStreamMaxRows) {
+        const float padded = (float)((n + HTM - 1) / HTM * HTM);
+        hot_flops += 2.f * padded * (float)p.K * (float)(GATED ? 2 * p.N : p.N);
+      }
+    }
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      cold_bytes += __shfl_xor(cold_bytes, off);
+      hot_flops += __shfl_xor(hot_flops, off);
+    }
+    if (lane == 0) {
+      work[0] = cold_bytes / (kColdCuGBps * 1e9f);
+      work[1] = hot_flops / (kHotCuTflops * 1e12f);
+    }
+  }
+  __syncthreads();
+  const int G = gridDim.x;
+  const float tc = work[0], th = work[1];
+  // X is a multiple of 8 so that both roles keep the rank -> XCD pairing their tile order
+  // relies on (block b runs on XCD b % 8)
+  int X = 0;
+  if (tc > 0.f) X = th > 0.f ? (int)(G * tc / (tc + th) / 8.f + 0.5f) * 8 : G;
+  if (tc > 0.f && X < 8) X = 8 < G ? 8 : G;
+  if (th > 0.f && X > G - 8) X = G - 8;
+  X = __builtin_amdgcn_readfirstlane(X);
+  __syncthreads();  // `work` is read by every thread before smem is reused
+  // consecutive block indices go to different XCDs, so the first X are spread over all of them
+  if ((int)blockIdx.x < X)
+    dl_tiles<WF, GATED, 16, CWN, 1, 8, CRING, CDK, true>(p, smem, blockIdx.x, X, 0, kStreamMaxRows);
+  else
+    dl_tiles<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false>(p, smem, blockIdx.x - X, G - X,
+                                                           kStreamMaxRows, 0x7fffffff);
+}
+
+template <int WF, bool GATED, int HWM, int HWN, int HRING, int HDK, int CWN, int CRING, int CDK>
+static hipError_t launch_prefill(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
+  const size_t lh = dl_lds_bytes<WF, HWM, HWN, 2, 4, HRING, HDK>(p);
+  const size_t lc = dl_lds_bytes<WF, 16, CWN, 1, 8, CRING, CDK>(p);
+  const size_t lds = lh > lc ? lh : lc;
+  auto kern = &ffn_prefill_kernel<WF, GATED, HWM, HWN, HRING, HDK, CWN, CRING, CDK>;
+  hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (st != hipSuccess) return st;
+  kern<<<dev.num_cus, 512, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
+          bool ASKIP = false>
 static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
   constexpr int NTH = 64 * WGM * WGN;
   constexpr int WB = WF == kFP8 ? 1 : 2;
@@ -1070,6 +1164,19 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.act == MOE_F32) {
     st = launch_stream<kF32, kF32, 2, 1, 1, 4>(gu, dev, stream);
     if (st == hipSuccess) st = launch_stream<kF32, kF32, 1, 2, 1, 4>(dn, dev, stream);
+    return st;
+  }
+  // prefill-sized batches: small and large experts in one launch per GEMM (ffn_prefill_kernel)
+  if (tiled && big && (a.wdt == MOE_BF16 || fp8_dl)) {
+    TiledArgs pgu = tgu, pdn = tdn;
+    pgu.min_rows = pdn.min_rows = 0;
+    if (a.wdt == MOE_BF16) {
+      st = launch_prefill<kBF16, true, 128, 64, 2, 64, 32, 4, 64>(pgu, dev, stream);
+      if (st == hipSuccess) st = launch_prefill<kBF16, false, 128, 64, 2, 64, 32, 4, 64>(pdn, dev, stream);
+    } else {
+      st = launch_prefill<kFP8, true, 64, 64, 2, 128, 32, 3, 128>(pgu, dev, stream);
+      if (st == hipSuccess) st = launch_prefill<kFP8, false, 64, 64, 2, 128, 32, 3, 128>(pdn, dev, stream);
+    }
     return st;
   }
   if (a.wdt == MOE_BF16) {

@@ -1141,10 +1141,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.rows == 0) return hipSuccess;
   // Which kernel takes which expert (decided per expert on the device from its row count):
   //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
-  //  - bf16/fp8 decode-sized batches (T*k < 32*E): bf16 weights go to the 64 x 128
-  //    direct-to-LDS tiles for every expert; fp8 weights stream experts with <= 16 rows and
-  //    tile the rest;
-  //  - prefill-sized batches: experts with <= 16 rows stream, the rest take 256-row tiles.
+  //  - decode-sized batches (T*k < 32*E): bf16 weights go to the 64 x 128 direct-to-LDS tiles
+  //    for every expert; fp8 weights stream experts with <= 16 rows and tile the rest;
+  //  - prefill-sized batches: one launch per GEMM whose workgroups split into a streaming role
+  //    (experts with <= 16 rows, 16 x 256 tiles) and a large-tile role (the rest).
   const bool tiled = a.act == MOE_BF16 && a.d % kTK == 0 && a.d_ff % kTK == 0;
   const bool big = (long long)a.rows >= 32LL * a.E;
   int small = tiled ? kStreamMaxRows : 0x7fffffff;
@@ -1157,7 +1157,6 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
                 a.E, a.d, a.d_ff, a.rows, small};
   TiledArgs tdn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
                 a.E, a.d_ff, a.d, a.rows, small};
-  const bool stream_pass = small > 0;
   // the fp8 direct-to-LDS kernel keeps an item's scale rows in LDS: 4 x 2 x K/128 floats
   const bool fp8_dl = big && a.d <= kFp8DlMaxK && a.d_ff <= kFp8DlMaxK;
   hipError_t st = hipSuccess;
@@ -1180,24 +1179,25 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
     return st;
   }
   if (a.wdt == MOE_BF16) {
-    if (stream_pass) st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
-    if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<kBF16, true, 128, 64, 2, 4, 2, 64>(tgu, dev, stream) : launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
-    if (st == hipSuccess && stream_pass) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
-    if (st == hipSuccess && tiled)
-      st = big ? launch_tiled_dl<kBF16, false, 128, 64, 2, 4, 2, 64>(tdn, dev, stream) : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
+    if (!tiled) {
+      st = launch_stream<kBF16, kBF16, 2, 2, 2, 4>(gu, dev, stream);
+      if (st == hipSuccess) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
+      return st;
+    }
+    st = launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
+    if (st == hipSuccess) st = launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
+  // fp8 weights outside the prefill kernel's range: small experts stream, the rest go to the
+  // register-staged tiles
   st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl ? launch_tiled_dl<kFP8, true, 64, 64, 2, 4, 2, 128>(tgu, dev, stream)
-                : (big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
-                       : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream));
+    st = big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
+             : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
   if (st == hipSuccess) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl ? launch_tiled_dl<kFP8, false, 64, 64, 2, 4, 2, 128>(tdn, dev, stream)
-                : (big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
-                       : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream));
+    st = big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
+             : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
   return st;
 }
 

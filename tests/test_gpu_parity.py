@@ -279,6 +279,21 @@ def test_identity_experts_through_permute_and_combine(dev):
     assert oracle.rel_max_err(out["y"].cpu().numpy(), x.astype(np.float64)) <= 1e-6
 
 
+@pytest.mark.parametrize("T,E,k", [(3, 4, 1), (16, 8, 2)])
+def test_decode_few_experts_long_contraction(dev, T, E, k):
+    # one to a few experts and a long contraction on the decode-sized path (fewer tiles than
+    # workgroups): the result matches the oracle and a second run bit for bit
+    cfg = synth.tiny_config(T=T, d=2048, E=E, k=k, d_ff=1024, act="bf16", w="bf16", seed=5)
+    assert cfg.T * cfg.k < 32 * cfg.E
+    got, _ = run_full(cfg, dev)
+    logits, x = synth.make_routing_inputs(cfg)
+    ids, _ = oracle.route(logits, cfg.k)
+    W = H.DeviceWeights(cfg, dev, experts=H.active_experts(np.bincount(ids.ravel(), minlength=cfg.E)))
+    again = H.run_layer(cfg, logits, x, W, dev)
+    for n in got:
+        assert np.array_equal(got[n].view(np.uint8), again[n].view(np.uint8)), n
+
+
 def test_repeat_runs_bit_identical(dev):
     cfg = synth.CONFIGS["c2"]
     logits, x = synth.make_routing_inputs(cfg)

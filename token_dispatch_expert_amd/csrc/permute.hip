@@ -59,18 +59,34 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
   __shared__ int32_t sc[kScanThreads];
   const int e = threadIdx.x;
   int total = 0;
+  // Up to kScanRegTiles tiles, every tile count of this expert is loaded at once (one memory
+  // latency) and kept in registers as its exclusive prefix until the expert base is known;
+  // longer batches take a loop of batched loads with the prefix written back to ws.
+  constexpr int kScanRegTiles = 64;
+  int pre[kScanRegTiles];
+  const bool in_regs = n_tiles <= kScanRegTiles;
   if (e < E) {
-    // exclusive prefix over tiles (batches of independent loads hide latency)
-    constexpr int B = 16;
-    for (int t0 = 0; t0 < n_tiles; t0 += B) {
-      int h[B];
+    if (in_regs) {
 #pragma unroll
-      for (int u = 0; u < B; ++u) h[u] = (t0 + u < n_tiles) ? ws[(size_t)(t0 + u) * E + e] : 0;
+      for (int u = 0; u < kScanRegTiles; ++u) pre[u] = u < n_tiles ? ws[(size_t)u * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        if (t0 + u < n_tiles) {
-          ws[(size_t)(t0 + u) * E + e] = total;
-          total += h[u];
+      for (int u = 0; u < kScanRegTiles; ++u) {
+        const int h = pre[u];
+        pre[u] = total;
+        total += h;
+      }
+    } else {
+      constexpr int B = 16;
+      for (int t0 = 0; t0 < n_tiles; t0 += B) {
+        int h[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) h[u] = (t0 + u < n_tiles) ? ws[(size_t)(t0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          if (t0 + u < n_tiles) {
+            ws[(size_t)(t0 + u) * E + e] = total;
+            total += h[u];
+          }
         }
       }
     }
@@ -88,7 +104,13 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
   const int excl = sc[threadIdx.x] - total;
   if (e < E) {
     offsets[e] = excl;
-    for (int t = 0; t < n_tiles; ++t) ws[(size_t)t * E + e] += excl;
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kScanRegTiles; ++u)
+        if (u < n_tiles) ws[(size_t)u * E + e] = pre[u] + excl;
+    } else {
+      for (int t = 0; t < n_tiles; ++t) ws[(size_t)t * E + e] += excl;
+    }
   }
   if (threadIdx.x == 0) offsets[E] = sc[kScanThreads - 1];
 }
@@ -110,10 +132,20 @@ __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __re
   __syncthreads();
   const int base = blockIdx.x * kPermuteTile;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int c = 0; c < kPermuteTile; c += kWave) {
+  // the tile's expert ids, all loaded before the walk (one memory latency, not one per chunk)
+  constexpr int kChunks = kPermuteTile / kWave;
+  int key[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = base + c * kWave + lane;
+    key[c] = i < R ? clamp_expert(ids[i], E) : 0;
+  }
+#pragma unroll
+  for (int cc = 0; cc < kChunks; ++cc) {
+    const int c = cc * kWave;
     const int i = base + c + lane;
     const bool valid = i < R;
-    const int e = valid ? clamp_expert(ids[i], E) : 0;
+    const int e = key[cc];
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;

@@ -68,8 +68,16 @@ def calibrate_copy(steps: int) -> None:
     log(f"copied {COPY_CAL_BYTES} bytes x {steps}")
 
 
+def _gpu_busy(us: float = 150.0) -> None:
+    """Keeps the GPU busy for about `us` microseconds (a spin kernel), so that the host can enqueue
+    a timed call before the GPU reaches it: the events then bracket GPU execution only."""
+    import torch
+    torch.cuda._sleep(int(us * 2.5e3))  # cycles at most ~2.5 GHz
+
+
 def _time_calls(fn, reps: int, warmup: int = 2) -> list:
-    """Per-call times in microseconds of fn() on the current stream (HIP events)."""
+    """Per-call times in microseconds of fn() on the current stream (HIP events), each call
+    enqueued behind a spin kernel so that host launch latency is not timed."""
     import torch
     for _ in range(warmup):
         fn()
@@ -77,6 +85,7 @@ def _time_calls(fn, reps: int, warmup: int = 2) -> list:
     out = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        _gpu_busy()
         a.record()
         fn()
         b.record()
@@ -400,31 +409,34 @@ def main() -> int:
     active = int(np.count_nonzero(counts))
     R = T * k
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     perm_ws = moe.Workspace(moe.moe_permute_workspace_size(T, E, k), device=dev)
     ffn_ws = moe.Workspace(moe.moe_ffn_workspace_size(R, E, d, d_ff, act_t, w_t), device=dev)
-    # every timed pass starts with cold caches: reading 512 MiB evicts the L2s and the 256 MB MALL
+    # every timed call starts with cold caches: reading 512 MiB evicts the L2s and the 256 MB MALL
     # (a read, so that no dirty lines are left to be written back inside the timed calls)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    samples = []
+    calls = [
+        lambda: moe.moe_route(logits, k, out["topk_ids"], out["topk_gates"]),
+        lambda: moe.moe_permute(x, out["topk_ids"], E, out["counts"], out["offsets"],
+                                out["sorted_to_flat"], out["flat_to_sorted"], out["x_sorted"], perm_ws),
+        lambda: moe.moe_grouped_ffn(out["x_sorted"], out["offsets"], W["gate"], W["up"], W["down"],
+                                    out["y_sorted"], ffn_ws, **skw),
+        lambda: moe.moe_combine(out["y_sorted"], out["flat_to_sorted"], out["topk_gates"], out["y"]),
+    ]
+    # Each call is timed on its own, on the inputs the layer steps above left in place (every call
+    # recomputes the same outputs). Nothing synchronises between the flush and the call: the host
+    # enqueues the call while the flush still runs (~140 us), so the events bracket the call's GPU
+    # execution and not the host's launch latency.
     reps = max(args.steps, 1)
-    for _ in range(reps):
-        flush.sum()
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        moe.moe_route(logits, k, out["topk_ids"], out["topk_gates"])
-        ev[1].record(stream)
-        moe.moe_permute(x, out["topk_ids"], E, out["counts"], out["offsets"], out["sorted_to_flat"],
-                        out["flat_to_sorted"], out["x_sorted"], perm_ws)
-        ev[2].record(stream)
-        moe.moe_grouped_ffn(out["x_sorted"], out["offsets"], W["gate"], W["up"], W["down"],
-                            out["y_sorted"], ffn_ws, **skw)
-        ev[3].record(stream)
-        moe.moe_combine(out["y_sorted"], out["flat_to_sorted"], out["topk_gates"], out["y"])
-        ev[4].record(stream)
-        torch.cuda.synchronize()
-        samples.append([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(4)])
-    samples = np.asarray(samples)  # [reps, 4] microseconds per call
+    samples = np.zeros((reps, len(calls)))
+    for i, fn in enumerate(calls):
+        for r in range(reps):
+            flush.sum()
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            samples[r, i] = ev[0].elapsed_time(ev[1]) * 1e3
     t_us = samples.mean(axis=0)
     pct = np.percentile(samples, [10, 50, 90], axis=0)
     a = 4 if cfg.act == "f32" else 2

@@ -155,8 +155,11 @@ moe_status_t moe_permute_capped(const void* x, moe_dtype_t x_dtype, const int32_
                                 int32_t* flat_to_sorted, void* x_sorted, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace moe_grouped_ffn needs (holds the SwiGLU activations h [rows, d_ff] in
- * act_dtype between the two GEMMs, plus a small schedule). */
+/* Bytes of workspace moe_grouped_ffn needs: the SwiGLU activations h [rows, d_ff] in act_dtype
+ * between the two GEMMs, and, for launches small enough that the contraction is split across
+ * workgroups (rows < 32 * E, bf16 activations and weights, and at most 256 tiles of 64 rows by
+ * 64 h columns, or by 128 output columns, counting every expert that could hold a row), 16 MiB
+ * of fp32 partial tiles after h. */
 size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_dtype,
                               moe_dtype_t w_dtype);
 

@@ -115,7 +115,11 @@ def test_ffn_rejects_bad_arguments(lib):
     f = lib.moe_grouped_ffn
     rows, E, d, d_ff = 128, 8, 256, 384
     wsb = lib.moe_ffn_workspace_size(rows, E, d, d_ff, B.MOE_BF16, B.MOE_BF16)
-    assert wsb == rows * d_ff * 2
+    # decode-sized bf16 launch with at most 256 tiles whatever the routing: 6 column tiles of 64
+    # h columns x (2 row tiles + 8 experts) = 60, so the partial tiles (512 x 64 x 128 fp32)
+    # follow h
+    split = 512 * 64 * 128 * 4
+    assert wsb == rows * d_ff * 2 + split
     base = dict(x=P, act=B.MOE_BF16, off=P2, rows=rows, E=E, d=d, d_ff=d_ff, wg=P, wu=P2, wd=P3,
                 wdt=B.MOE_BF16, sg=None, su=None, sd=None, y=P, ws=P2, wsb=wsb, s=None)
 
@@ -149,6 +153,20 @@ def test_combine_and_layer_reject_bad_arguments(lib):
     args[-2] = need
     args[2] = B.MOE_FP8_E4M3FN
     assert lib.moe_layer(*args) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_ffn_workspace_split_rule(lib):
+    f = lib.moe_ffn_workspace_size
+    split = 512 * 64 * 128 * 4
+    # one decode token routed to 8 of 128 experts (d=4096, d_ff=1536): gate/up has at most
+    # 24 x (1 + 8) = 216 tiles -> split
+    assert f(8, 128, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 8 * 1536 * 2 + split
+    # 1024 rows over 128 experts: up to 24 x (16 + 128) tiles -> no split
+    assert f(1024, 128, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 1024 * 1536 * 2
+    # prefill-sized (rows >= 32 E), fp8 weights and fp32 never split
+    assert f(4096, 8, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 4096 * 1536 * 2
+    assert f(8, 128, 4096, 1536, B.MOE_BF16, B.MOE_FP8_E4M3FN) == 8 * 1536 * 2
+    assert f(8, 128, 4096, 1536, B.MOE_F32, B.MOE_F32) == 8 * 1536 * 4
 
 
 def test_workspace_sizes(lib):

@@ -474,6 +474,10 @@ struct TiledArgs {
   const int32_t* offsets;
   int E, K, N, rows;
   int min_rows;  // experts with at most this many rows are left to the streaming kernel
+  // contraction split of launches with few tiles: fp32 partial tiles, and the grid of the launch
+  // that computes them (both launches derive the chunk count from it)
+  float* partial = nullptr;
+  int split_ranks = 0;
 };
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN>
@@ -734,6 +738,11 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
                                            voffset, soffset, 0, 0);
 }
 constexpr int kRing = 4;    // LDS ring depth
+// contraction split (decode-sized launches with few tiles): at most kSplitMaxUnits chunks, each
+// with a partial tile of kSplitTileElems fp32 values
+constexpr int kSplitMaxUnits = 512;
+constexpr int kSplitTileElems = 64 * 128;
+constexpr int kSplitMaxChunks = 16;  // the sum keeps one fragment's chunks in registers
 
 // LDS image of a tile row of CPR chunks of 16 bytes: chunk c of row r sits at chunk c ^ x(r),
 // x(r) = (r >> 2) & 3 for 4 chunks, (r >> 1) & 7 for 8 and r & 15 for 16, so that the 16 rows
@@ -763,6 +772,36 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   wait_vmcnt_dyn_impl(n, std::make_integer_sequence<int, MAX + 1>{});
 }
 
+// Epilogue of one tile: rows below nrows and columns below N of the accumulator tile go out;
+// the gated GEMM writes h = silu(gate) * up in bf16, the other one fp32.
+template <bool GATED, int WM, int WN, int MF, int NF>
+__device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32x4 (&acc)[MF][NF],
+                                                   int wm, int wn, int lane, int r0, int nrows,
+                                                   int c0) {
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr) {
+      const int r = wm * WM + mf * 16 + (lane >> 4) * 4 + jr;
+      if (r >= nrows) continue;
+      const size_t orow = (size_t)(r0 + r) * p.N;
+      if constexpr (GATED) {
+#pragma unroll
+        for (int nf = 0; nf < NF / 2; ++nf) {
+          const int col = c0 + wn * (WN / 2) + nf * 16 + (lane & 15);
+          if (col < p.N)
+            static_cast<__bf16*>(p.out)[orow + col] = (__bf16)(silu(acc[mf][nf][jr]) * acc[mf][nf + NF / 2][jr]);
+        }
+      } else {
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+          const int col = c0 + wn * WN + nf * 16 + (lane & 15);
+          if (col < p.N) static_cast<float*>(p.out)[orow + col] = acc[mf][nf][jr];
+        }
+      }
+    }
+}
+
 // WF: weight format, kBF16 or kFP8 (e4m3fn with fp32 scales per 128 x 128 block). fp8 weights
 // go to LDS as bytes and are widened to bf16 exactly after the fragment load; the MFMAs of one
 // 128-long contraction block accumulate into a partial tile that is then added to the
@@ -770,12 +809,18 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // exact fp8 products' fp32 sum, never a rounded weight). fp8 needs DK = 64.
 // The tile loop of one workgroup, which is rank `rank` of `nranks` workgroups sharing the
 // tiles of the experts with more than min_rows and at most max_rows rows.
+// MODE 0 runs whole tiles. With few tiles, MODE 1 cuts each tile's contraction into S chunks
+// of consecutive steps, one per workgroup, and stores each chunk's fp32 partial tile; MODE 2 (a
+// second launch) adds a tile's S partials in chunk order and applies the epilogue, so the result
+// does not depend on timing and needs no synchronisation inside a launch.
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
-          bool ASKIP = false>
+          bool ASKIP = false, int MODE = 0>
 __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem, int rank,
                                          int nranks, int min_rows, int max_rows) {
   static_assert(DK == 32 || DK == 64 || DK == 128, "contraction step");
   static_assert(WF == kBF16 || (WF == kFP8 && DK >= 64), "weight format");
+  static_assert(MODE == 0 || (WF == kBF16 && !ASKIP && WGM * WM * WGN * WN <= kSplitTileElems),
+                "contraction split: bf16 weights, every row loaded, tiles of at most 64 x 128");
   constexpr bool F8 = WF == kFP8;
   constexpr int WB = F8 ? 1 : 2;                        // weight bytes per element
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
@@ -812,15 +857,18 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
   const size_t wstride = (size_t)p.N * p.K * WB;  // bytes per expert matrix
   const int NB = p.N / 128, KBn = p.K / 128;     // fp8 scale blocks
 
-  for (int base = 0; base < total; base += nranks) {
-    const int item = xcd_round_item(base, total, rank, nranks);
-    if (item < 0) continue;  // uniform per workgroup
+  auto tile_epilogue = [&](const TiledArgs& pp, const f32x4 (&a)[MF][NF], int wm_, int wn_, int lane_,
+                           int r0_, int nrows_, int c0_) __attribute__((always_inline)) {
+    tile_epilogue_impl<GATED, WM, WN, MF, NF>(pp, a, wm_, wn_, lane_, r0_, nrows_, c0_);
+  };
+  // tile of item `item`: expert, first row, rows, first column
+  auto tile_of = [&](int item, int& e, int& r0, int& nrows, int& c0) __attribute__((always_inline)) {
     int lo = 0, hi = p.E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (__builtin_amdgcn_readfirstlane(pre[mid]) <= item) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
+    e = lo;
     const int local = item - __builtin_amdgcn_readfirstlane(pre[e]);
     constexpr int kGroupM = 4;
     const int ebeg = __builtin_amdgcn_readfirstlane(offs[e]);
@@ -830,9 +878,57 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
     const int j = local - g * kGroupM * NT;
     const int nt = j / gm;
     const int mt = g * kGroupM + j % gm;
-    const int r0 = ebeg + mt * TM;
-    const int nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
-    const int c0 = nt * cols_per_tile;
+    r0 = ebeg + mt * TM;
+    nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
+    c0 = nt * cols_per_tile;
+  };
+
+  // contraction split: S chunks per tile (at least 2 steps each), so that the tile count times S
+  // fits the split launch's grid and the partial buffer; the same in both split launches
+  int S = 1;
+  if constexpr (MODE != 0) {
+    const int units_max = min(kSplitMaxUnits, p.split_ranks);
+    S = max(1, min(min(kSplitMaxChunks, max(1, nst / 2)), units_max / max(total, 1)));
+  }
+  constexpr int kSlot = MF * NF * 4 * NTH;  // floats of one partial tile, in register order
+  // partial tile fragment (mf, nf) of thread tid sits at ((mf * NF + nf) * NTH + tid) * 4
+  if constexpr (MODE == 2) {
+    for (int item = rank; item < total; item += nranks) {
+      int e, r0, nrows, c0;
+      tile_of(item, e, r0, nrows, c0);
+      f32x4 acc[MF][NF];
+      const float* first = p.partial + (size_t)item * S * kSlot;
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+          f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (wm * WM + mf * 16 < nrows) {  // fragments of absent rows hold nothing
+            // every chunk's load is in flight before the sum, which then goes in chunk order
+            f32x4 v[kSplitMaxChunks];
+#pragma unroll
+            for (int c = 0; c < kSplitMaxChunks; ++c)
+              if (c < S)
+                v[c] = *reinterpret_cast<const f32x4*>(first + (size_t)c * kSlot + ((mf * NF + nf) * NTH + tid) * 4);
+#pragma unroll
+            for (int c = 0; c < kSplitMaxChunks; ++c)
+              if (c < S) sum += v[c];
+          }
+          acc[mf][nf] = sum;
+        }
+      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0);
+    }
+    return;
+  }
+
+  const int units = total * S;
+  for (int base = 0; base < units; base += nranks) {
+    const int unit = xcd_round_item(base, units, rank, nranks);
+    if (unit < 0) continue;  // uniform per workgroup
+    const int item = unit / S, chunk = unit % S;
+    const int st_lo = chunk * nst / S, st_hi = (chunk + 1) * nst / S;
+    int e, r0, nrows, c0;
+    tile_of(item, e, r0, nrows, c0);
     // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
     // issued, and the 16-row fragments past it take no LDS reads and no MFMAs: those LDS rows
     // keep stale data, which could only reach accumulator rows that are never stored (row r of
@@ -922,10 +1018,10 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
 
 #pragma unroll
     for (int st = 0; st < RING - 1; ++st)
-      if (st < nst) issue(st);
-    for (int st = 0; st < nst; ++st) {
+      if (st_lo + st < st_hi) issue(st_lo + st);
+    for (int st = st_lo; st < st_hi; ++st) {
       // this wave's loads of step st are done once at most the later steps' loads are pending
-      const int later = min(RING - 2, nst - 1 - st);
+      const int later = min(RING - 2, st_hi - 1 - st);
       wait_vmcnt_dyn<(RING - 2) * LPW>(later * lpw);
       // every wave's loads of step st have landed (the wait above) and every wave is done
       // reading the slot of step st-1. A bare s_barrier: a fence here would make the compiler
@@ -959,7 +1055,7 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
         }
         // the next loads go out after this slice's fragment reads: DMA writes landing in LDS
         // while the reads are in progress slow both down
-        if (h == 0 && st + RING - 1 < nst) issue(st + RING - 1);
+        if (h == 0 && st + RING - 1 < st_hi) issue(st + RING - 1);
         // one slice's fragments live at a time: the compiler may not hoist the next slice's
         // reads above these MFMAs (that would need registers the big tile does not have)
         if (DK / 32 > 1) __builtin_amdgcn_sched_barrier(0);
@@ -992,38 +1088,27 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
       }
     }
     __syncthreads();  // all waves done reading the ring before the next item refills it
-
+    if constexpr (MODE == 1) {
+      float* mine = p.partial + ((size_t)item * S + chunk) * kSlot;
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+      for (int mf = 0; mf < MF; ++mf) {
+        if (wm * WM + mf * 16 >= nrows) continue;  // absent rows: nothing to keep
 #pragma unroll
-      for (int jr = 0; jr < 4; ++jr) {
-        const int r = wm * WM + mf * 16 + (lane >> 4) * 4 + jr;
-        if (r >= nrows) continue;
-        const size_t orow = (size_t)(r0 + r) * p.N;
-        if constexpr (GATED) {
-#pragma unroll
-          for (int nf = 0; nf < NF / 2; ++nf) {
-            const int col = c0 + wn * (WN / 2) + nf * 16 + (lane & 15);
-            if (col < p.N)
-              static_cast<__bf16*>(p.out)[orow + col] = (__bf16)(silu(acc[mf][nf][jr]) * acc[mf][nf + NF / 2][jr]);
-          }
-        } else {
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            const int col = c0 + wn * WN + nf * 16 + (lane & 15);
-            if (col < p.N) static_cast<float*>(p.out)[orow + col] = acc[mf][nf][jr];
-          }
-        }
+        for (int nf = 0; nf < NF; ++nf)
+          *reinterpret_cast<f32x4*>(mine + ((mf * NF + nf) * NTH + tid) * 4) = acc[mf][nf];
       }
+    } else {
+      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0);
+    }
   }
 }
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
-          bool ASKIP = false>
+          bool ASKIP = false, int MODE = 0>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  dl_tiles<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP>(p, smem, blockIdx.x, gridDim.x, p.min_rows,
-                                                         0x7fffffff);
+  dl_tiles<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP, MODE>(p, smem, blockIdx.x, gridDim.x,
+                                                               p.min_rows, 0x7fffffff);
 }
 
 // LDS bytes of dl_tiles for a tile shape (prefix arrays, ring, fp8 scale rows)
@@ -1131,10 +1216,52 @@ static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hip
   return hipGetLastError();
 }
 
+// Decode-sized bf16 launches whose tile count is small whatever the routing (at most
+// kSplitMaxUnits / 2 tiles of 64 rows x cols_per_tile columns, bounded with every expert that
+// can hold a row active) split the contraction across workgroups; the host decides from the
+// sizes alone, and the workspace holds the partial tiles after h.
+static bool split_gemm(int rows, int E, int N, int cols_per_tile) {
+  const long long nt = (N + cols_per_tile - 1) / cols_per_tile;
+  const long long tiles = nt * ((rows + 63) / 64 + (long long)(E < rows ? E : rows));
+  return tiles <= kSplitMaxUnits / 2;
+}
+static bool decode_tiled_bf16(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
+  return act == MOE_BF16 && wdt == MOE_BF16 && d % kTK == 0 && d_ff % kTK == 0 &&
+         (long long)rows < 32LL * E;
+}
+static bool uses_split(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
+  return decode_tiled_bf16(rows, E, d, d_ff, act, wdt) &&
+         (split_gemm(rows, E, d_ff, 64) || split_gemm(rows, E, d, 128));
+}
+constexpr size_t kPartialBytes = (size_t)kSplitMaxUnits * kSplitTileElems * sizeof(float);
+
 size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
-  (void)E; (void)d; (void)wdt;
   const size_t hb = act == MOE_F32 ? 4 : 2;
-  return align_up((size_t)rows * d_ff * hb, 256);
+  const size_t h = align_up((size_t)rows * d_ff * hb, 256);
+  return uses_split(rows, E, d, d_ff, act, wdt) ? h + kPartialBytes : h;
+}
+
+// The split pair of one GEMM: chunk partials, then the in-order sum and epilogue.
+template <bool GATED>
+static hipError_t launch_split(TiledArgs p, const DeviceInfo& dev, hipStream_t stream) {
+  constexpr int WM = 32, WN = 64, WGM = 2, WGN = 2, RING = 3, DK = 64, NTH = 64 * WGM * WGN;
+  const size_t lds = dl_lds_bytes<kBF16, WM, WN, WGM, WGN, RING, DK>(p);
+  const int fit = (int)((160 * 1024) / lds);
+  const int grid = dev.num_cus * (fit < 1 ? 1 : (fit > 4 ? 4 : fit));
+  p.split_ranks = grid;
+  auto k1 = &ffn_tiled_dl_kernel<kBF16, GATED, WM, WN, WGM, WGN, RING, DK, false, 1>;
+  if (lds > 64 * 1024) {
+    hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (st != hipSuccess) return st;
+  }
+  k1<<<grid, NTH, lds, stream>>>(p);
+  hipError_t st = hipGetLastError();
+  if (st != hipSuccess) return st;
+  // the sum needs only the item prefix in LDS
+  const size_t lds2 = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + ((NTH + 3) & ~3)) * sizeof(int32_t);
+  ffn_tiled_dl_kernel<kBF16, GATED, WM, WN, WGM, WGN, RING, DK, false, 2><<<grid, NTH, lds2, stream>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream) {
@@ -1184,8 +1311,16 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
       if (st == hipSuccess) st = launch_stream<kBF16, kBF16, 1, 4, 2, 4>(dn, dev, stream);
       return st;
     }
-    st = launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
-    if (st == hipSuccess) st = launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
+    // launches with few tiles whatever the routing split the contraction (partials in the
+    // workspace after h)
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(a.h) +
+                                              align_up((size_t)a.rows * a.d_ff * 2, 256));
+    tgu.partial = tdn.partial = partial;
+    st = split_gemm(a.rows, a.E, a.d_ff, 64) ? launch_split<true>(tgu, dev, stream)
+                                             : launch_tiled_dl<kBF16, true, 32, 64, 2, 2, 3, 64>(tgu, dev, stream);
+    if (st == hipSuccess)
+      st = split_gemm(a.rows, a.E, a.d, 128) ? launch_split<false>(tdn, dev, stream)
+                                             : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
   // fp8 weights outside the prefill kernel's range: small experts stream, the rest go to the

@@ -279,10 +279,13 @@ def test_identity_experts_through_permute_and_combine(dev):
     assert oracle.rel_max_err(out["y"].cpu().numpy(), x.astype(np.float64)) <= 1e-6
 
 
-@pytest.mark.parametrize("T,E,k", [(3, 4, 1), (16, 8, 2)])
+@pytest.mark.parametrize("T,E,k", [(3, 4, 1), (16, 8, 2), (60, 2, 1)])
 def test_decode_few_experts_long_contraction(dev, T, E, k):
-    # one to a few experts and a long contraction on the decode-sized path (fewer tiles than
-    # workgroups): the result matches the oracle and a second run bit for bit
+    # one to a few experts and a long contraction on the decode-sized path with so few tiles
+    # that each tile's contraction is cut into chunks on different workgroups (up to 16 chunks
+    # of at least 2 steps) whose fp32 partials a second launch adds in chunk order; (60, 2, 1) routes 36
+    # and 24 rows, so both 32-row halves of a tile carry rows. The result matches the oracle and
+    # a second run bit for bit.
     cfg = synth.tiny_config(T=T, d=2048, E=E, k=k, d_ff=1024, act="bf16", w="bf16", seed=5)
     assert cfg.T * cfg.k < 32 * cfg.E
     got, _ = run_full(cfg, dev)

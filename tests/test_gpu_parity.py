@@ -128,6 +128,13 @@ def test_single_token(dev, act, w):
     run_full(synth.tiny_config(T=1, d=128, E=8, k=2, d_ff=256, act=act, w=w, seed=3), dev)
 
 
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_single_token_full_width(dev, name):
+    # one decode token at the full layer widths: each GEMM has few enough tiles that its
+    # contraction is split across workgroups and summed by a second launch
+    run_full(synth.CONFIGS[name].with_(T=1, name=f"{name}-T1"), dev)
+
+
 def test_k_equals_e(dev):
     run_full(synth.tiny_config(T=33, d=64, E=4, k=4, d_ff=96, act="bf16", w="bf16", seed=4), dev)
 

@@ -36,6 +36,13 @@ size_t permute_workspace_ints(int T, int E, int k) {
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
+// word 3 of a raw buffer descriptor on gfx950 (32-bit elements, no swizzle, bounds-checked);
+// entry j of the tile through `rsrc`, 0 past its extent
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ int load_tile_id(__amdgpu_buffer_rsrc_t rsrc, int j) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rsrc, j * 4, 0, 0);
+}
+
 __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ ids, int R,
                                                            int E, int32_t* __restrict__ ws) {
   extern __shared__ int32_t hist[];
@@ -129,17 +136,23 @@ __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __re
     run[e] = bases[e];
     lim[e] = offsets[e + 1];
   }
-  __syncthreads();
+  // One wavefront per workgroup: its LDS accesses take effect in program order, so no barrier
+  // is needed between the writes above and the reads below, nor between a chunk's reads of the
+  // running positions and their update (a workgroup barrier would also wait for this wave's
+  // global stores of the index maps, once per chunk). The wave barriers only keep the compiler
+  // from moving LDS accesses across them.
+  __builtin_amdgcn_wave_barrier();
   const int base = blockIdx.x * kPermuteTile;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  // the tile's expert ids, all loaded before the walk (one memory latency, not one per chunk)
+  // the tile's expert ids, all loaded before the walk (one memory latency, not one per chunk):
+  // buffer loads through a descriptor that ends at the batch's last entry read zeros past it,
+  // so the loads carry no condition that the compiler could turn into a branch around each
+  const __amdgpu_buffer_rsrc_t tile_ids = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ids + base), (short)0, (int)(min(R - base, kPermuteTile) * 4), kRawBufferWord3);
   constexpr int kChunks = kPermuteTile / kWave;
   int key[kChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int i = base + c * kWave + lane;
-    key[c] = i < R ? clamp_expert(ids[i], E) : 0;
-  }
+  for (int c = 0; c < kChunks; ++c) key[c] = clamp_expert(load_tile_id(tile_ids, c * kWave + lane), E);
 #pragma unroll
   for (int cc = 0; cc < kChunks; ++cc) {
     const int c = cc * kWave;
@@ -158,10 +171,10 @@ __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __re
       if (pos < lim[e]) s2f[pos] = i;
       f2s[i] = pos < lim[e] ? pos : -1;
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     // the highest lane of each group of equal experts advances that expert's base
     if (valid && (63 - __clzll(same)) == lane) run[e] += __popcll(same);
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
 }
 

@@ -185,10 +185,23 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   const int t = blockIdx.x;
   const int32_t* pos = f2s + (size_t)t * k;
   const uint4* src = x + (size_t)t * vec_per_row;
-  for (int v = threadIdx.x; v < vec_per_row; v += blockDim.x) {
-    const uint4 val = src[v];
-    for (int j = 0; j < k; ++j)
-      if (pos[j] >= 0) xs[(size_t)pos[j] * vec_per_row + v] = val;  // -1: dropped slot
+  constexpr int U = 4;  // a thread's loads in flight before its stores
+  for (int v0 = threadIdx.x; v0 < vec_per_row; v0 += U * blockDim.x) {
+    uint4 val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * blockDim.x;
+      val[u] = v < vec_per_row ? src[v] : make_uint4(0, 0, 0, 0);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int p = pos[j];
+      if (p < 0) continue;  // dropped slot
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < vec_per_row) xs[(size_t)p * vec_per_row + v] = val[u];
+      }
+    }
   }
 }
 
@@ -246,14 +259,29 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
     total = min(total, cap);  // kept assignments (capacity factor)
     counts[tid] = total;
   }
-  sc[tid] = total;
-  __syncthreads();
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-    const int v = tid >= off ? sc[tid - off] : 0;
-    __syncthreads();
-    sc[tid] += v;
-    __syncthreads();
+  // inclusive scan of the capped counts over the 1024 threads: within each wave by shuffles,
+  // then the 16 wave totals by one wave (three barriers instead of a 20-barrier LDS scan)
+  int v = total;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
   }
+  __shared__ int32_t wave_sum[kSmallWaves];
+  if (lane == kWave - 1) wave_sum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kSmallWaves ? wave_sum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kSmallWaves; off <<= 1) {
+      const int t = __shfl_up(w, off);
+      if (lane >= off) w += t;
+    }
+    if (lane < kSmallWaves) wave_sum[lane] = w;
+  }
+  __syncthreads();
+  sc[tid] = v + (wave > 0 ? wave_sum[wave - 1] : 0);
+  __syncthreads();
   if (tid < E) {
     const int base = sc[tid] - total;
     offsets[tid] = base;

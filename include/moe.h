@@ -159,7 +159,9 @@ moe_status_t moe_permute_capped(const void* x, moe_dtype_t x_dtype, const int32_
  * between the two GEMMs, and, for launches small enough that the contraction is split across
  * workgroups (rows < 32 * E, bf16 activations and weights, and at most 256 tiles of 64 rows by
  * 64 h columns, or by 128 output columns, counting every expert that could hold a row), 16 MiB
- * of fp32 partial tiles after h. */
+ * of fp32 partial tiles after h; for prefill-sized launches (rows >= 32 * E, bf16 activations,
+ * bf16 or fp8 weights) a 256-byte header and 64 MiB (bf16) or 32 MiB (fp8) of fp32 partial
+ * tiles for the last round's tiles, whose contraction is split across workgroups. */
 size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_dtype,
                               moe_dtype_t w_dtype);
 

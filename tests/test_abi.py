@@ -163,10 +163,13 @@ def test_ffn_workspace_split_rule(lib):
     assert f(8, 128, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 8 * 1536 * 2 + split
     # 1024 rows over 128 experts: up to 24 x (16 + 128) tiles -> no split
     assert f(1024, 128, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 1024 * 1536 * 2
-    # prefill-sized (rows >= 32 E), fp8 weights and fp32 never split
-    assert f(4096, 8, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 4096 * 1536 * 2
+    # decode-sized fp8 weights and fp32 never split
     assert f(8, 128, 4096, 1536, B.MOE_BF16, B.MOE_FP8_E4M3FN) == 8 * 1536 * 2
     assert f(8, 128, 4096, 1536, B.MOE_F32, B.MOE_F32) == 8 * 1536 * 4
+    # prefill-sized (rows >= 32 E): a 256-byte header and 256 partial tiles of the hot tile
+    # (256 x 256 fp32 with bf16 weights, 128 x 256 with fp8) for the last round's split tiles
+    assert f(4096, 8, 4096, 1536, B.MOE_BF16, B.MOE_BF16) == 4096 * 1536 * 2 + 256 + 256 * 256 * 256 * 4
+    assert f(4096, 8, 4096, 1536, B.MOE_BF16, B.MOE_FP8_E4M3FN) == 4096 * 1536 * 2 + 256 + 256 * 128 * 256 * 4
 
 
 def test_workspace_sizes(lib):
@@ -174,7 +177,8 @@ def test_workspace_sizes(lib):
     assert lib.moe_permute_workspace_size(8192, 256, 8) == 64 * 256 * 4
     assert lib.moe_permute_workspace_size(0, 256, 8) == 0
     assert lib.moe_permute_workspace_size(5, 4, 9) == 0           # invalid -> 0
-    assert lib.moe_ffn_workspace_size(65536, 256, 7168, 2048, B.MOE_BF16, B.MOE_FP8_E4M3FN) == 65536 * 2048 * 2
+    assert lib.moe_ffn_workspace_size(65536, 256, 7168, 2048, B.MOE_BF16, B.MOE_FP8_E4M3FN) == \
+        65536 * 2048 * 2 + 256 + 256 * 128 * 256 * 4
     assert lib.moe_ffn_workspace_size(128, 8, 128, 256, B.MOE_F32, B.MOE_F32) == 128 * 256 * 4
 
 

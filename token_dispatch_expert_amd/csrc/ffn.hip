@@ -478,6 +478,9 @@ struct TiledArgs {
   // that computes them (both launches derive the chunk count from it)
   float* partial = nullptr;
   int split_ranks = 0;
+  // tail split of prefill launches: {S, first split item, end of the split items}, written by
+  // the launch that computes the chunks and read by the one that adds them
+  int32_t* split_info = nullptr;
 };
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN>
@@ -743,6 +746,7 @@ constexpr int kRing = 4;    // LDS ring depth
 constexpr int kSplitMaxUnits = 512;
 constexpr int kSplitTileElems = 64 * 128;
 constexpr int kSplitMaxChunks = 16;  // the sum keeps one fragment's chunks in registers
+constexpr int kTailMaxUnits = 256;   // chunks of a prefill launch's last round
 
 // LDS image of a tile row of CPR chunks of 16 bytes: chunk c of row r sits at chunk c ^ x(r),
 // x(r) = (r >> 2) & 3 for 4 chunks, (r >> 1) & 7 for 8 and r & 15 for 16, so that the 16 rows
@@ -777,11 +781,12 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 template <bool GATED, int WM, int WN, int MF, int NF>
 __device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32x4 (&acc)[MF][NF],
                                                    int wm, int wn, int lane, int r0, int nrows,
-                                                   int c0) {
+                                                   int c0, int mf_only) {
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
     for (int jr = 0; jr < 4; ++jr) {
+      if (mf_only >= 0 && mf != mf_only) continue;  // another unit's fragment rows
       const int r = wm * WM + mf * 16 + (lane >> 4) * 4 + jr;
       if (r >= nrows) continue;
       const size_t orow = (size_t)(r0 + r) * p.N;
@@ -819,8 +824,9 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
                                          int nranks, int min_rows, int max_rows) {
   static_assert(DK == 32 || DK == 64 || DK == 128, "contraction step");
   static_assert(WF == kBF16 || (WF == kFP8 && DK >= 64), "weight format");
-  static_assert(MODE == 0 || (WF == kBF16 && !ASKIP && WGM * WM * WGN * WN <= kSplitTileElems),
-                "contraction split: bf16 weights, every row loaded, tiles of at most 64 x 128");
+  static_assert(MODE == 0 || !ASKIP, "contraction split: every row loaded");
+  static_assert(MODE != 1 || (WF == kBF16 && WGM * WM * WGN * WN <= kSplitTileElems),
+                "decode contraction split: bf16 weights, tiles of at most 64 x 128");
   constexpr bool F8 = WF == kFP8;
   constexpr int WB = F8 ? 1 : 2;                        // weight bytes per element
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
@@ -852,14 +858,14 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
   constexpr int cols_per_tile = GATED ? TN / 2 : TN;
   const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
   build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, max_rows, NT, offs, min_rows, TM);
-  const int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
+  int total = __builtin_amdgcn_readfirstlane(pre[p.E]);
   const int nst = p.K / DK;  // K is a multiple of 64 (of 128 for fp8) on this path
   const size_t wstride = (size_t)p.N * p.K * WB;  // bytes per expert matrix
   const int NB = p.N / 128, KBn = p.K / 128;     // fp8 scale blocks
 
   auto tile_epilogue = [&](const TiledArgs& pp, const f32x4 (&a)[MF][NF], int wm_, int wn_, int lane_,
-                           int r0_, int nrows_, int c0_) __attribute__((always_inline)) {
-    tile_epilogue_impl<GATED, WM, WN, MF, NF>(pp, a, wm_, wn_, lane_, r0_, nrows_, c0_);
+                           int r0_, int nrows_, int c0_, int mf_only = -1) __attribute__((always_inline)) {
+    tile_epilogue_impl<GATED, WM, WN, MF, NF>(pp, a, wm_, wn_, lane_, r0_, nrows_, c0_, mf_only);
   };
   // tile of item `item`: expert, first row, rows, first column
   auto tile_of = [&](int item, int& e, int& r0, int& nrows, int& c0) __attribute__((always_inline)) {
@@ -885,25 +891,56 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
 
   // contraction split: S chunks per tile (at least 2 steps each), so that the tile count times S
   // fits the split launch's grid and the partial buffer; the same in both split launches
-  int S = 1;
-  if constexpr (MODE != 0) {
+  // Tail split (MODE 3, prefill): the rounds in which every workgroup has a tile run whole
+  // tiles; the tiles of the last, partial round (first_split .. total) are cut into S chunks
+  // so that the round keeps every workgroup busy, and a second launch (MODE 2) adds them.
+  int S = 1, first_split = 0;
+  if constexpr (MODE == 1) {
     const int units_max = min(kSplitMaxUnits, p.split_ranks);
     S = max(1, min(min(kSplitMaxChunks, max(1, nst / 2)), units_max / max(total, 1)));
+  } else if constexpr (MODE == 2) {
+    if (p.split_info) {
+      // the header of the launch before: accepted only if its chunks fit the partial buffer
+      // (anything else is treated as no split)
+      S = p.split_info[0];
+      first_split = p.split_info[1];
+      const int end = p.split_info[2];
+      const bool ok = S >= 1 && S <= kSplitMaxChunks && first_split >= 0 && end >= first_split &&
+                      end <= total && (long long)(end - first_split) * S <= kTailMaxUnits;
+      if (!ok) { S = 1; first_split = total; }
+      else total = end;  // items past the split range were finished whole
+    } else {
+      const int units_max = min(kSplitMaxUnits, p.split_ranks);
+      S = max(1, min(min(kSplitMaxChunks, max(1, nst / 2)), units_max / max(total, 1)));
+    }
+  } else if constexpr (MODE == 3) {
+    first_split = total / nranks * nranks;
+    const int R = total - first_split;
+    if (R > 0) S = max(1, min(min(kSplitMaxChunks, max(1, nst / 2)), min(nranks, kTailMaxUnits) / R));
+    if (S == 1) first_split = total;  // nothing to split
+    if (rank == 0 && tid == 0 && p.split_info) {
+      p.split_info[0] = S;
+      p.split_info[1] = first_split;
+      p.split_info[2] = S > 1 ? total : first_split;
+    }
   }
   constexpr int kSlot = MF * NF * 4 * NTH;  // floats of one partial tile, in register order
   // partial tile fragment (mf, nf) of thread tid sits at ((mf * NF + nf) * NTH + tid) * 4
   if constexpr (MODE == 2) {
-    for (int item = rank; item < total; item += nranks) {
+    // one unit per (tile, 16-row fragment index): a tile's chunks are added by MF workgroups
+    for (int u = rank; u < (total - first_split) * MF; u += nranks) {
+      const int item = first_split + u / MF, mfu = u % MF;
       int e, r0, nrows, c0;
       tile_of(item, e, r0, nrows, c0);
       f32x4 acc[MF][NF];
-      const float* first = p.partial + (size_t)item * S * kSlot;
+      const float* first = p.partial + (size_t)(item - first_split) * S * kSlot;
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
           f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (wm * WM + mf * 16 < nrows) {  // fragments of absent rows hold nothing
+          // fragments of absent rows hold nothing; other fragment rows belong to other units
+          if (mf == mfu && wm * WM + mf * 16 < nrows) {
             // every chunk's load is in flight before the sum, which then goes in chunk order
             f32x4 v[kSplitMaxChunks];
 #pragma unroll
@@ -916,17 +953,20 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
           }
           acc[mf][nf] = sum;
         }
-      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0);
+      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0, mfu);
     }
     return;
   }
 
-  const int units = total * S;
+  // units: whole tiles first (MODE 0 and 3), then S chunks per split tile
+  const int units = first_split + (total - first_split) * S;
   for (int base = 0; base < units; base += nranks) {
     const int unit = xcd_round_item(base, units, rank, nranks);
     if (unit < 0) continue;  // uniform per workgroup
-    const int item = unit / S, chunk = unit % S;
-    const int st_lo = chunk * nst / S, st_hi = (chunk + 1) * nst / S;
+    const bool split = unit >= first_split && S > 1;
+    const int item = split ? first_split + (unit - first_split) / S : unit;
+    const int chunk = split ? (unit - first_split) % S : 0;
+    const int st_lo = split ? chunk * nst / S : 0, st_hi = split ? (chunk + 1) * nst / S : nst;
     int e, r0, nrows, c0;
     tile_of(item, e, r0, nrows, c0);
     // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
@@ -1088,8 +1128,8 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
       }
     }
     __syncthreads();  // all waves done reading the ring before the next item refills it
-    if constexpr (MODE == 1) {
-      float* mine = p.partial + ((size_t)item * S + chunk) * kSlot;
+    if (MODE == 1 || (MODE == 3 && split)) {
+      float* mine = p.partial + ((size_t)(item - first_split) * S + chunk) * kSlot;
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
         if (wm * WM + mf * 16 >= nrows) continue;  // absent rows: nothing to keep
@@ -1175,12 +1215,18 @@ __global__ __launch_bounds__(512) void ffn_prefill_kernel(TiledArgs p) {
   if (th > 0.f && X > G - 8) X = G - 8;
   X = __builtin_amdgcn_readfirstlane(X);
   __syncthreads();  // `work` is read by every thread before smem is reused
+  // no hot role: an empty tail-split header for the launch that adds the chunks
+  if (X >= G && blockIdx.x == 0 && threadIdx.x == 0 && p.split_info) {
+    p.split_info[0] = 1;
+    p.split_info[1] = 0;
+    p.split_info[2] = 0;
+  }
   // consecutive block indices go to different XCDs, so the first X are spread over all of them
   if ((int)blockIdx.x < X)
     dl_tiles<WF, GATED, 16, CWN, 1, 8, CRING, CDK, true>(p, smem, blockIdx.x, X, 0, kStreamMaxRows);
   else
-    dl_tiles<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false>(p, smem, blockIdx.x - X, G - X,
-                                                           kStreamMaxRows, 0x7fffffff);
+    dl_tiles<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 3>(p, smem, blockIdx.x - X, G - X,
+                                                              kStreamMaxRows, 0x7fffffff);
 }
 
 template <int WF, bool GATED, int HWM, int HWN, int HRING, int HDK, int CWN, int CRING, int CDK>
@@ -1193,6 +1239,14 @@ static hipError_t launch_prefill(const TiledArgs& p, const DeviceInfo& dev, hipS
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (st != hipSuccess) return st;
   kern<<<dev.num_cus, 512, lds, stream>>>(p);
+  st = hipGetLastError();
+  if (st != hipSuccess) return st;
+  // the tail split's chunks, added in chunk order (a launch of its own: the kernel boundary
+  // orders the partial tiles' stores before these loads); only the item prefix in LDS
+  TiledArgs q = p;
+  q.min_rows = kStreamMaxRows;
+  const size_t lds2 = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + 512) * sizeof(int32_t);
+  ffn_tiled_dl_kernel<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 2><<<dev.num_cus, 512, lds2, stream>>>(q);
   return hipGetLastError();
 }
 
@@ -1235,10 +1289,23 @@ static bool uses_split(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dt
 }
 constexpr size_t kPartialBytes = (size_t)kSplitMaxUnits * kSplitTileElems * sizeof(float);
 
+// Prefill-sized launches run ffn_prefill_kernel, whose last round's tiles may be split: a
+// 256-byte header and kTailMaxUnits partial tiles of the hot tile size follow h.
+static bool prefill_tiled(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
+  return act == MOE_BF16 && d % kTK == 0 && d_ff % kTK == 0 && (long long)rows >= 32LL * E &&
+         (wdt == MOE_BF16 || (wdt == MOE_FP8_E4M3FN && d <= kFp8DlMaxK && d_ff <= kFp8DlMaxK));
+}
+constexpr size_t kHotTileElemsBF16 = 256 * 256, kHotTileElemsFP8 = 128 * 256;
+static size_t tail_partial_bytes(moe_dtype_t wdt) {
+  return 256 + (size_t)kTailMaxUnits * (wdt == MOE_BF16 ? kHotTileElemsBF16 : kHotTileElemsFP8) * sizeof(float);
+}
+
 size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
   const size_t hb = act == MOE_F32 ? 4 : 2;
   const size_t h = align_up((size_t)rows * d_ff * hb, 256);
-  return uses_split(rows, E, d, d_ff, act, wdt) ? h + kPartialBytes : h;
+  if (uses_split(rows, E, d, d_ff, act, wdt)) return h + kPartialBytes;
+  if (prefill_tiled(rows, E, d, d_ff, act, wdt)) return h + tail_partial_bytes(wdt);
+  return h;
 }
 
 // The split pair of one GEMM: chunk partials, then the in-order sum and epilogue.
@@ -1296,6 +1363,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (tiled && big && (a.wdt == MOE_BF16 || fp8_dl)) {
     TiledArgs pgu = tgu, pdn = tdn;
     pgu.min_rows = pdn.min_rows = 0;
+    // tail-split header and partial tiles after h (shared by the two GEMMs, which run in order)
+    char* tail = static_cast<char*>(a.h) + align_up((size_t)a.rows * a.d_ff * 2, 256);
+    pgu.split_info = pdn.split_info = reinterpret_cast<int32_t*>(tail);
+    pgu.partial = pdn.partial = reinterpret_cast<float*>(tail + 256);
     if (a.wdt == MOE_BF16) {
       st = launch_prefill<kBF16, true, 128, 64, 2, 64, 32, 4, 64>(pgu, dev, stream);
       if (st == hipSuccess) st = launch_prefill<kBF16, false, 128, 64, 2, 64, 32, 4, 64>(pdn, dev, stream);

@@ -781,7 +781,7 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 template <bool GATED, int WM, int WN, int MF, int NF>
 __device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32x4 (&acc)[MF][NF],
                                                    int wm, int wn, int lane, int r0, int nrows,
-                                                   int c0, int mf_only) {
+                                                   int c0, int mf_only, int nf_only) {
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
@@ -793,6 +793,7 @@ __device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32
       if constexpr (GATED) {
 #pragma unroll
         for (int nf = 0; nf < NF / 2; ++nf) {
+          if (nf_only >= 0 && nf != nf_only) continue;
           const int col = c0 + wn * (WN / 2) + nf * 16 + (lane & 15);
           if (col < p.N)
             static_cast<__bf16*>(p.out)[orow + col] = (__bf16)(silu(acc[mf][nf][jr]) * acc[mf][nf + NF / 2][jr]);
@@ -800,6 +801,7 @@ __device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32
       } else {
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
+          if (nf_only >= 0 && nf != nf_only) continue;
           const int col = c0 + wn * WN + nf * 16 + (lane & 15);
           if (col < p.N) static_cast<float*>(p.out)[orow + col] = acc[mf][nf][jr];
         }
@@ -864,8 +866,8 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
   const int NB = p.N / 128, KBn = p.K / 128;     // fp8 scale blocks
 
   auto tile_epilogue = [&](const TiledArgs& pp, const f32x4 (&a)[MF][NF], int wm_, int wn_, int lane_,
-                           int r0_, int nrows_, int c0_, int mf_only = -1) __attribute__((always_inline)) {
-    tile_epilogue_impl<GATED, WM, WN, MF, NF>(pp, a, wm_, wn_, lane_, r0_, nrows_, c0_, mf_only);
+                           int r0_, int nrows_, int c0_, int mf_only = -1, int nf_only = -1) __attribute__((always_inline)) {
+    tile_epilogue_impl<GATED, WM, WN, MF, NF>(pp, a, wm_, wn_, lane_, r0_, nrows_, c0_, mf_only, nf_only);
   };
   // tile of item `item`: expert, first row, rows, first column
   auto tile_of = [&](int item, int& e, int& r0, int& nrows, int& c0) __attribute__((always_inline)) {
@@ -927,9 +929,11 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
   constexpr int kSlot = MF * NF * 4 * NTH;  // floats of one partial tile, in register order
   // partial tile fragment (mf, nf) of thread tid sits at ((mf * NF + nf) * NTH + tid) * 4
   if constexpr (MODE == 2) {
-    // one unit per (tile, 16-row fragment index): a tile's chunks are added by MF workgroups
-    for (int u = rank; u < (total - first_split) * MF; u += nranks) {
-      const int item = first_split + u / MF, mfu = u % MF;
+    // one unit per (tile, 16-row fragment index, 16-column fragment index; gated tiles keep
+    // a gate column fragment and its up partner together): MF * NFU workgroups per tile
+    constexpr int NFU = GATED ? NF / 2 : NF;
+    for (int u = rank; u < (total - first_split) * MF * NFU; u += nranks) {
+      const int item = first_split + u / (MF * NFU), mfu = (u / NFU) % MF, nfu = u % NFU;
       int e, r0, nrows, c0;
       tile_of(item, e, r0, nrows, c0);
       f32x4 acc[MF][NF];
@@ -939,8 +943,8 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
           f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-          // fragments of absent rows hold nothing; other fragment rows belong to other units
-          if (mf == mfu && wm * WM + mf * 16 < nrows) {
+          // fragments of absent rows hold nothing; other fragments belong to other units
+          if (mf == mfu && (nf == nfu || (GATED && nf == nfu + NF / 2)) && wm * WM + mf * 16 < nrows) {
             // every chunk's load is in flight before the sum, which then goes in chunk order
             f32x4 v[kSplitMaxChunks];
 #pragma unroll
@@ -953,7 +957,7 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
           }
           acc[mf][nf] = sum;
         }
-      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0, mfu);
+      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0, mfu, nfu);
     }
     return;
   }

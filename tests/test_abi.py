@@ -173,8 +173,8 @@ def test_ffn_workspace_split_rule(lib):
 
 
 def test_workspace_sizes(lib):
-    # one int32 per (tile of 1024 assignments, expert), rounded up to 256 bytes
-    assert lib.moe_permute_workspace_size(8192, 256, 8) == 64 * 256 * 4
+    # one int32 per (tile of 256 assignments, expert), rounded up to 256 bytes
+    assert lib.moe_permute_workspace_size(8192, 256, 8) == 256 * 256 * 4
     assert lib.moe_permute_workspace_size(0, 256, 8) == 0
     assert lib.moe_permute_workspace_size(5, 4, 9) == 0           # invalid -> 0
     assert lib.moe_ffn_workspace_size(65536, 256, 7168, 2048, B.MOE_BF16, B.MOE_FP8_E4M3FN) == \

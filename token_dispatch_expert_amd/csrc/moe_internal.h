@@ -21,7 +21,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // plain 16-byt
 constexpr int kWave = 64;
 
 // Permutation tiles: flat assignments are processed in tiles of this many entries.
-constexpr int kPermuteTile = 1024;
+constexpr int kPermuteTile = 256;
 
 // Grouped-FFN streaming kernel geometry (see ffn.hip).
 constexpr int kStreamWaves = 4;     // waves per workgroup; they split the contraction axis

@@ -16,8 +16,9 @@
 // deterministic (smaller batches use one workgroup for the first three, see
 // permute_small_kernel):
 //   hist : one workgroup per tile of kPermuteTile flat entries; LDS histogram -> ws[tile][e]
-//   scan : one workgroup; per expert an exclusive prefix over tiles, then counts, the
-//          exclusive scan over experts (offsets) and per-tile bases ws[tile][e]
+//   scan : one workgroup; per expert an exclusive prefix over tiles (groups of threads take
+//          ranges of tiles), then counts, the exclusive scan over experts (offsets) and
+//          per-tile bases ws[tile][e]
 //   rank : one wavefront per tile walks its entries in flat order, 64 at a time; lanes with
 //          the same expert find each other with ballots over the expert id's bits, so a
 //          lane's rank among equal keys is a popcount of lower lanes; the group's last lane
@@ -58,68 +59,109 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
 }
 
 constexpr int kScanThreads = 1024;  // >= MOE_MAX_EXPERTS
+constexpr int kScanRegTiles = 64;   // tile counts one scan thread keeps in registers
 
+// Inclusive prefix sum of v over the 1024 threads of the workgroup: shuffles within each wave,
+// then the 16 wave totals by one wave.
+__device__ __forceinline__ int block_inclusive_scan_1024(int v, int32_t* wave_sum) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  constexpr int kWaves = kScanThreads / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  if (lane == kWave - 1) wave_sum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kWaves ? wave_sum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWaves; off <<= 1) {
+      const int t = __shfl_up(w, off);
+      if (lane >= off) w += t;
+    }
+    if (lane < kWaves) wave_sum[lane] = w;
+  }
+  __syncthreads();
+  return v + (wave > 0 ? wave_sum[wave - 1] : 0);
+}
+
+// The 1024 threads are G groups of E (G = 1024 / E, at most the tile count); group g takes a
+// contiguous range of tiles, so thread (g, e) scans at most kScanRegTiles tile counts of expert
+// e in registers (all loaded at once). Group totals give each group's base per expert; the
+// expert totals, capped, are scanned over the experts for the offsets.
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ ws,
                                                                     int n_tiles, int E, int cap,
                                                                     int32_t* __restrict__ counts,
                                                                     int32_t* __restrict__ offsets) {
-  __shared__ int32_t sc[kScanThreads];
-  const int e = threadIdx.x;
-  int total = 0;
-  // Up to kScanRegTiles tiles, every tile count of this expert is loaded at once (one memory
-  // latency) and kept in registers as its exclusive prefix until the expert base is known;
-  // longer batches take a loop of batched loads with the prefix written back to ws.
-  constexpr int kScanRegTiles = 64;
+  __shared__ int32_t gsum[kScanThreads];  // [G][E] group totals
+  __shared__ int32_t expert_off[kScanThreads];
+  __shared__ int32_t wave_sum[kScanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int G = max(1, min(kScanThreads / E, n_tiles));
+  const int g = tid / E, e = tid - g * E;
+  const bool active = g < G;
+  const int tpg = (n_tiles + G - 1) / G;
+  const int t0 = min(g * tpg, n_tiles), t1 = min(t0 + tpg, n_tiles);
+  const bool in_regs = tpg <= kScanRegTiles;
   int pre[kScanRegTiles];
-  const bool in_regs = n_tiles <= kScanRegTiles;
-  if (e < E) {
+  int run = 0;  // exclusive prefix within the group, then the group total
+  if (active) {
     if (in_regs) {
 #pragma unroll
-      for (int u = 0; u < kScanRegTiles; ++u) pre[u] = u < n_tiles ? ws[(size_t)u * E + e] : 0;
+      for (int u = 0; u < kScanRegTiles; ++u) pre[u] = t0 + u < t1 ? ws[(size_t)(t0 + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < kScanRegTiles; ++u) {
         const int h = pre[u];
-        pre[u] = total;
-        total += h;
+        pre[u] = run;
+        run += h;
       }
     } else {
-      constexpr int B = 16;
-      for (int t0 = 0; t0 < n_tiles; t0 += B) {
+      constexpr int B = 16;  // batches of independent loads
+      for (int tb = t0; tb < t1; tb += B) {
         int h[B];
 #pragma unroll
-        for (int u = 0; u < B; ++u) h[u] = (t0 + u < n_tiles) ? ws[(size_t)(t0 + u) * E + e] : 0;
+        for (int u = 0; u < B; ++u) h[u] = (tb + u < t1) ? ws[(size_t)(tb + u) * E + e] : 0;
 #pragma unroll
         for (int u = 0; u < B; ++u) {
-          if (t0 + u < n_tiles) {
-            ws[(size_t)(t0 + u) * E + e] = total;
-            total += h[u];
+          if (tb + u < t1) {
+            ws[(size_t)(tb + u) * E + e] = run;
+            run += h[u];
           }
         }
       }
     }
-    total = min(total, cap);  // kept assignments (capacity factor)
-    counts[e] = total;
+    gsum[tid] = run;
   }
-  sc[threadIdx.x] = total;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
-    __syncthreads();
-    sc[threadIdx.x] += v;
-    __syncthreads();
+  int gbase = 0, total = 0;
+  if (active) {
+    for (int gg = 0; gg < G; ++gg) {
+      const int v = gsum[gg * E + e];
+      gbase += gg < g ? v : 0;
+      total += v;
+    }
   }
-  const int excl = sc[threadIdx.x] - total;
-  if (e < E) {
-    offsets[e] = excl;
+  // threads 0..E-1 are group 0: one per expert
+  const int kept = tid < E ? min(total, cap) : 0;  // kept assignments (capacity factor)
+  const int incl = block_inclusive_scan_1024(kept, wave_sum);
+  if (tid < E) {
+    counts[tid] = kept;
+    offsets[tid] = incl - kept;
+    expert_off[tid] = incl - kept;
+  }
+  if (tid == kScanThreads - 1) offsets[E] = incl;
+  __syncthreads();
+  if (active) {
+    const int base = expert_off[e] + gbase;
     if (in_regs) {
 #pragma unroll
       for (int u = 0; u < kScanRegTiles; ++u)
-        if (u < n_tiles) ws[(size_t)u * E + e] = pre[u] + excl;
+        if (t0 + u < t1) ws[(size_t)(t0 + u) * E + e] = pre[u] + base;
     } else {
-      for (int t = 0; t < n_tiles; ++t) ws[(size_t)t * E + e] += excl;
+      for (int t = t0; t < t1; ++t) ws[(size_t)t * E + e] += base;
     }
   }
-  if (threadIdx.x == 0) offsets[E] = sc[kScanThreads - 1];
 }
 
 __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __restrict__ ids,
@@ -213,6 +255,7 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
 constexpr int kSmallWaves = 16;
 constexpr int kSmallChunks = 8;  // 64-entry chunks per wave -> R <= 16 * 8 * 64
 constexpr int kSmallR = kSmallWaves * kSmallChunks * kWave;
+static_assert(kSmallWaves * kWave == kScanThreads, "the small kernel's scan is the 1024-thread one");
 
 __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
     const int32_t* __restrict__ ids, int R, int E, int nbits, int cap, int32_t* __restrict__ counts,
@@ -259,28 +302,9 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
     total = min(total, cap);  // kept assignments (capacity factor)
     counts[tid] = total;
   }
-  // inclusive scan of the capped counts over the 1024 threads: within each wave by shuffles,
-  // then the 16 wave totals by one wave (three barriers instead of a 20-barrier LDS scan)
-  int v = total;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
+  // inclusive scan of the capped counts over the 1024 threads (three barriers)
   __shared__ int32_t wave_sum[kSmallWaves];
-  if (lane == kWave - 1) wave_sum[wave] = v;
-  __syncthreads();
-  if (wave == 0) {
-    int w = lane < kSmallWaves ? wave_sum[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kSmallWaves; off <<= 1) {
-      const int t = __shfl_up(w, off);
-      if (lane >= off) w += t;
-    }
-    if (lane < kSmallWaves) wave_sum[lane] = w;
-  }
-  __syncthreads();
-  sc[tid] = v + (wave > 0 ? wave_sum[wave - 1] : 0);
+  sc[tid] = block_inclusive_scan_1024(total, wave_sum);
   __syncthreads();
   if (tid < E) {
     const int base = sc[tid] - total;

@@ -4,9 +4,7 @@
 // its own contiguous rows; all experts in one grouped launch) with the SwiGLU expert
 // h = silu(x Wg) * (x Wu), y = h Wd. The makespan-dispatcher abstract (on the page titled
 // UltraEP) measures two regimes: with few rows per expert the time is spent streaming the
-// expert's weights from HBM; with many rows it is GEMM tiles. This file holds the streaming
-// kernel: every weight byte of an expert with rows is read once per 32-row group, straight
-// from HBM into MFMA operand registers, with no padding of rows to a large M tile.
+// expert's weights from HBM; with many rows it is GEMM tiles.
 //
 // Data layout: weights are stored contraction-contiguous ([E, N, K] row-major: gate/up
 // N = d_ff, K = d; down N = d, K = d_ff), activations are [rows, K] row-major. The gfx950
@@ -14,13 +12,19 @@
 // elements (L/16)*8..+7 of row/column L%16, so each lane's fragment is one 16-byte load
 // (8-byte for fp8, 2x16-byte for fp32 with 16x16x4 f32 MFMA).
 //
-// Work decomposition: an item is (expert e, 32-row group mg, column block nb of NF*16
-// columns [x2 for gate and up]). A workgroup of 4 waves processes one item at a time from a
-// device-side item list (persistent grid); the waves split the contraction axis in 128-wide
-// blocks, keep one block of loads in flight while the previous block feeds the MFMAs, and
-// reduce their partial tiles through LDS in a fixed order (deterministic). The epilogue
-// applies SwiGLU and rounds h to the activation format (gate/up pass) or writes fp32
-// y_sorted (down pass).
+// Kernels (launch_grouped_ffn at the end picks them from the sizes; each expert's rows go to
+// one of them from its row count, decided on the device):
+//  - ffn_stream_kernel: weights straight from HBM into MFMA operand registers, 16-row items,
+//    the contraction split over the 4 waves and reduced through LDS in a fixed order; fp32,
+//    widths not multiples of 64, and experts with <= 16 rows in decode-sized fp8 launches.
+//  - dl_tiles (in ffn_tiled_dl_kernel and ffn_prefill_kernel): tiles loaded straight into a
+//    ring of LDS slots by buffer loads, XOR-swizzled for conflict-free fragment reads, on a
+//    persistent grid whose rounds of tiles are dealt to the XCDs in runs; decode-sized bf16
+//    launches (64 x 128 tiles, with a contraction split when there are few tiles) and, in
+//    ffn_prefill_kernel, both roles of prefill-sized launches: workgroups streaming the experts
+//    with <= 16 rows beside workgroups running 256-row tiles of the others.
+//  - ffn_tiled_kernel: the older register-staged tiles, for fp8 weights in decode-sized
+//    launches.
 //
 // fp8 weights (OCP e4m3fn, fp32 scale per 128x128 block): codes are converted exactly to bf16
 // in registers, each 128-long contraction block is accumulated from zero in fp32 and then
@@ -813,13 +817,16 @@ __device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32
 // go to LDS as bytes and are widened to bf16 exactly after the fragment load; the MFMAs of one
 // 128-long contraction block accumulate into a partial tile that is then added to the
 // accumulator times the block's scale (identical dequantisation: the scale multiplies the
-// exact fp8 products' fp32 sum, never a rounded weight). fp8 needs DK = 64.
+// exact fp8 products' fp32 sum, never a rounded weight). fp8 needs DK >= 64 (a scale block is
+// one or two steps).
 // The tile loop of one workgroup, which is rank `rank` of `nranks` workgroups sharing the
 // tiles of the experts with more than min_rows and at most max_rows rows.
 // MODE 0 runs whole tiles. With few tiles, MODE 1 cuts each tile's contraction into S chunks
-// of consecutive steps, one per workgroup, and stores each chunk's fp32 partial tile; MODE 2 (a
-// second launch) adds a tile's S partials in chunk order and applies the epilogue, so the result
-// does not depend on timing and needs no synchronisation inside a launch.
+// of consecutive steps, one per workgroup, and stores each chunk's fp32 partial tile; MODE 3
+// runs the rounds in which every workgroup has a tile whole and cuts only the last, partial
+// round's tiles that way. MODE 2 (a second launch) adds a tile's S partials in chunk order and
+// applies the epilogue, so the result does not depend on timing and needs no synchronisation
+// inside a launch.
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false, int MODE = 0>
 __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem, int rank,

@@ -21,21 +21,16 @@ oracle takes the readings listed below (each is also listed in the design notes)
   R2 gates: softmax restricted to the k chosen logits (the same as a full softmax
      renormalised over the top k), g_j = exp(l_j - l_max) / sum_i exp(l_i - l_max).
   R3 order inside an expert: stable in the flat index i = t*k + j.
-  R4 expert FFN: SwiGLU, y = (silu(x Wg) * (x Wu)) Wd with silu(z) = z / (1 + exp(-z)),
+  R4, R5 expert FFN: SwiGLU, y = (silu(x Wg) * (x Wu)) Wd with silu(z) = z / (1 + exp(-z)),
      no biases; weights are stored with the contraction axis contiguous (gate/up as
      [d_ff, d], down as [d, d_ff]), so x Wg is x @ gate.T here.
-  R5 fp8 weights: OCP e4m3fn codes times an fp32 scale per 128x128 block of the stored
+  R6 fp8 weights: OCP e4m3fn codes times an fp32 scale per 128x128 block of the stored
      matrix, decoded exactly to fp64.
-  R6 combine: fp64, summed in slot order j = 0..k-1; no token dropping.
   R7 (optional, off by default) h_round="bf16": h is rounded to the nearest bf16 between the
      two GEMMs, the rounding point of a bf16 implementation; tests use it as a second,
      tighter comparison next to the plain fp64 one.
-  R9 router scores (the fused router's input side; same page, section 4: the router decides
-     each token's experts): logits[t, e] = sum_i x[t, i] * w_router[e, i], one weight row per
-     expert, no bias or scaling; exact decode, fp64. The top-k of the fused GPU router is
-     checked by routing the GPU's own fp32 logits with `route` (a selection decided in floating
-     point is compared in the precision that decided it), and those logits against these.
-  R8 capacity factor (optional; same page, section 5, mitigation 1, and section 10, exercise
+  R8 combine: fp64, summed in slot order j = 0..k-1.
+  R9 capacity factor (optional; same page, section 5, mitigation 1, and section 10, exercise
      D): each expert keeps at most `capacity` assignments and the excess is dropped. The page
      states capacity = C * tokens / E; with k > 1 the count is of assignments, so
      capacity = ceil(C * T * k / E). The kept assignments of an expert are its first
@@ -43,6 +38,11 @@ oracle takes the readings listed below (each is also listed in the design notes)
      (flat_to_sorted = -1) and adds nothing in the combine (the token passes the expert by,
      the residual connection being outside the layer); the gates are not renormalised. The
      factor is taken in percent, so the capacity is exact integer arithmetic.
+  R14 router scores (the fused router's input side; same page, section 4: the router decides
+     each token's experts): logits[t, e] = sum_i x[t, i] * w_router[e, i], one weight row per
+     expert, no bias or scaling; exact decode, fp64. The top-k of the fused GPU router is
+     checked by routing the GPU's own fp32 logits with `route` (a selection decided in floating
+     point is compared in the precision that decided it), and those logits against these.
 Everything is fp64 after an exact decode of the stored inputs; there is no blocking, fusion
 or reordering beyond the steps above. Library primitives used as steps: numpy argmax (first
 occurrence of the maximum), fp64 matrix products (BLAS) and exp.
@@ -79,7 +79,7 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
 
 def decode_matrix(w: np.ndarray, fmt: str, scale: np.ndarray | None = None,
                   block: int = 128) -> np.ndarray:
-    """Stored matrix -> fp64 values (reading R5 for fp8: code value times its block's scale)."""
+    """Stored matrix -> fp64 values (reading R6 for fp8: code value times its block's scale)."""
     if fmt == F32:
         return np.asarray(w, dtype=np.float32).astype(np.float64)
     if fmt == BF16:
@@ -127,7 +127,7 @@ def route(logits: np.ndarray, k: int):
 
 
 def router_logits(x: np.ndarray, x_fmt: str, w_router: np.ndarray, w_fmt: str) -> np.ndarray:
-    """Router scores [T, E] = X W_r^T in fp64 from the exactly decoded stored values (R9)."""
+    """Router scores [T, E] = X W_r^T in fp64 from the exactly decoded stored values (R14)."""
     X = decode_activations(x, x_fmt)
     Wr = decode_matrix(w_router, w_fmt)
     return X @ Wr.T
@@ -137,14 +137,14 @@ def router_logits(x: np.ndarray, x_fmt: str, w_router: np.ndarray, w_fmt: str) -
 # permute: count, exclusive scan, stable scatter, row copy (tutorial section 4, dispatch)
 # ----------------------------------------------------------------------------------------
 def expert_capacity(T: int, E: int, k: int, factor_percent: int) -> int:
-    """capacity = ceil(C * T * k / E) assignments per expert (reading R8), with the factor
+    """capacity = ceil(C * T * k / E) assignments per expert (reading R9), with the factor
     C given in percent (C = 1.25 -> 125) so that the value is exact integer arithmetic."""
     return -(-(int(factor_percent) * T * k) // (100 * E))
 
 
 def permute(topk_ids: np.ndarray, E: int, capacity: int | None = None):
     """Stable counting sort of the flat assignments i = t*k + j by expert id (reading R3);
-    with a capacity, each expert keeps only its first `capacity` assignments (reading R8).
+    with a capacity, each expert keeps only its first `capacity` assignments (reading R9).
 
     Returns dict(counts int32 [E] (kept assignments), offsets int32 [E+1],
     sorted_to_flat int32 [offsets[E]], flat_to_sorted int32 [R], -1 where dropped)."""
@@ -238,11 +238,11 @@ def ffn(x_sorted: np.ndarray, offsets: np.ndarray, expert_weights, return_h: boo
 
 
 # ----------------------------------------------------------------------------------------
-# combine (tutorial section 4, combine; reading R6)
+# combine (tutorial section 4, combine; reading R8)
 # ----------------------------------------------------------------------------------------
 def combine(y_sorted: np.ndarray, flat_to_sorted: np.ndarray, gates: np.ndarray) -> np.ndarray:
     """y[t] = sum_j gates[t, j] * y_sorted[flat_to_sorted[t*k + j]], slot order, fp64; a
-    dropped slot (flat_to_sorted = -1, reading R8) adds nothing."""
+    dropped slot (flat_to_sorted = -1, reading R9) adds nothing."""
     T, k = gates.shape
     y = np.zeros((T, y_sorted.shape[1]), dtype=np.float64)
     for t in range(T):
@@ -270,7 +270,7 @@ def make_weight_decoder(raw_weights, w_fmt: str):
 
 def layer(logits, x, x_fmt: str, raw_weights, w_fmt: str, k: int, return_h: bool = False,
           h_round: str | None = None, capacity: int | None = None):
-    """The whole layer: route -> permute (optionally capped, R8) -> grouped FFN -> combine.
+    """The whole layer: route -> permute (optionally capped, R9) -> grouped FFN -> combine.
     Returns every intermediate."""
     T, E = np.asarray(logits).shape
     ids, gates = route(logits, k)

@@ -304,6 +304,27 @@ def test_decode_few_experts_long_contraction(dev, T, E, k):
         assert np.array_equal(got[n].view(np.uint8), again[n].view(np.uint8)), n
 
 
+@pytest.mark.parametrize("T,d,E,k,d_ff,act,w,zipf", [
+    (5, 1024, 16, 2, 512, "bf16", "bf16", 1.0),        # decode, contraction split of both GEMMs
+    (40, 512, 4, 2, 768, "bf16", "bf16", None),        # decode split, 14-27 rows per expert
+    (200, 256, 6, 3, 384, "bf16", "bf16", 1.2),        # prefill, every tile in a split last round
+    (300, 384, 5, 2, 640, "bf16", "bf16", None),       # prefill, last round split in 3
+    (700, 512, 8, 2, 512, "bf16", "fp8_e4m3fn", 1.0),  # fp8 prefill, last round split
+    (33, 200, 7, 3, 72, "f32", "f32", None),           # fp32 streaming
+])
+def test_ffn_paths_and_splits(dev, T, d, E, k, d_ff, act, w, zipf):
+    # the kernel paths the sizes select, including both contraction splits, against the oracle,
+    # and a second run bit for bit (the split sums go in chunk order)
+    cfg = synth.tiny_config(T=T, d=d, E=E, k=k, d_ff=d_ff, act=act, w=w, zipf_s=zipf, seed=21)
+    got, _ = run_full(cfg, dev)
+    logits, x = synth.make_routing_inputs(cfg)
+    ids, _ = oracle.route(logits, cfg.k)
+    W = H.DeviceWeights(cfg, dev, experts=H.active_experts(np.bincount(ids.ravel(), minlength=cfg.E)))
+    again = H.run_layer(cfg, logits, x, W, dev)
+    for n in got:
+        assert np.array_equal(got[n].view(np.uint8), again[n].view(np.uint8)), n
+
+
 def test_repeat_runs_bit_identical(dev):
     cfg = synth.CONFIGS["c2"]
     logits, x = synth.make_routing_inputs(cfg)

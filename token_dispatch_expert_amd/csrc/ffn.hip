@@ -8,9 +8,10 @@
 //
 // Data layout: weights are stored contraction-contiguous ([E, N, K] row-major: gate/up
 // N = d_ff, K = d; down N = d, K = d_ff), activations are [rows, K] row-major. The gfx950
-// MFMA operand layout v_mfma_f32_16x16x32_bf16 gives lane L the 8 consecutive contraction
-// elements (L/16)*8..+7 of row/column L%16, so each lane's fragment is one 16-byte load
-// (8-byte for fp8, 2x16-byte for fp32 with 16x16x4 f32 MFMA).
+// MFMA operand layout v_mfma_f32_16x16x32_bf16 gives lane L 8 contraction elements of
+// row/column L%16 (the same 8 for both operands; which 8 of the 32 is the kernel's choice), so
+// each lane's fragment is one 16-byte load (fp8 weights: 8 bytes, or 16 bytes serving two
+// MFMAs; fp32: 2x16 bytes with the 16x16x4 f32 MFMA).
 //
 // Kernels (launch_grouped_ffn at the end picks them from the sizes; each expert's rows go to
 // one of them from its row count, decided on the device):
@@ -718,11 +719,14 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 // Tiled kernel with direct-to-LDS operand loads (bf16 or fp8 weights). Same tile decomposition
 // as ffn_tiled_kernel, but operands go from memory straight into LDS (buffer loads into LDS, 16
 // bytes per lane, no register staging) through a ring of RING contraction steps of DK
-// elements, keeping RING-1 steps of loads in flight while the MFMAs consume the oldest one.
+// elements. A step's slot is refilled as soon as every wave holds the fragments of the step's
+// last 32-wide slice in registers, and the fragment reads of each slice overlap the MFMAs of
+// the one before, so the MFMA pipe waits neither on LDS reads nor on the barrier's refill.
 // Shapes:
 //  - prefill, 256 x 256 tiles, DK = 64, 2 slots (128 KB): the operands mostly hit in L2, one
-//    barrier per 64-wide step (half as many as with 32-wide steps measured 7% faster), the next
-//    step's loads in flight while the MFMAs consume the current one;
+//    barrier per 64-wide step (32-wide steps in 4 slots, twice the barriers with 1.5x the bytes
+//    in flight, measured 9% slower), the next step's loads in flight while the MFMAs consume
+//    the current one;
 //  - decode, 64 x 128 tiles, DK = 64, 3 slots, two workgroups per CU: weight streaming, where
 //    each weight row is read a full 128-byte line per step (64-byte pieces of many rows
 //    measured ~15% below line-sized ones in HBM throughput);
@@ -730,7 +734,7 @@ static hipError_t launch_tiled(const TiledArgs& p, const DeviceInfo& dev, hipStr
 //    (8.5% faster than 64-wide steps in 4 slots).
 // The loading lanes pick their source addresses so that the linear LDS image is the swizzled
 // tile (see dswz).
-constexpr int kDK = 32;     // contraction step
+constexpr int kDK = 64;     // contraction step
 constexpr int kFp8DlMaxK = 65536;  // longest contraction of the fp8 direct-to-LDS kernel
 // Word 3 of a raw buffer descriptor (32-bit data format, bounds-checked offsets): loads at or
 // past num_records bytes return zeros.
@@ -769,6 +773,19 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 // the same with a wave-uniform runtime count in [0, MAX] (a scalar branch per candidate)
 template <int... Ns>
@@ -831,7 +848,7 @@ template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing
           bool ASKIP = false, int MODE = 0>
 __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem, int rank,
                                          int nranks, int min_rows, int max_rows) {
-  static_assert(DK == 32 || DK == 64 || DK == 128, "contraction step");
+  static_assert(DK == 64 || DK == 128, "contraction step: an even number of 32-wide slices");
   static_assert(WF == kBF16 || (WF == kFP8 && DK >= 64), "weight format");
   static_assert(MODE == 0 || !ASKIP, "contraction split: every row loaded");
   static_assert(MODE != 1 || (WF == kBF16 && WGM * WM * WGN * WN <= kSplitTileElems),
@@ -1067,76 +1084,130 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
       __syncthreads();
     }
 
-#pragma unroll
-    for (int st = 0; st < RING - 1; ++st)
-      if (st_lo + st < st_hi) issue(st_lo + st);
-    for (int st = st_lo; st < st_hi; ++st) {
-      // this wave's loads of step st are done once at most the later steps' loads are pending
-      const int later = min(RING - 2, st_hi - 1 - st);
-      wait_vmcnt_dyn<(RING - 2) * LPW>(later * lpw);
-      // every wave's loads of step st have landed (the wait above) and every wave is done
-      // reading the slot of step st-1. A bare s_barrier: a fence here would make the compiler
-      // drain all outstanding direct-to-LDS loads. The signal fences only stop the compiler
-      // from moving LDS accesses across the barrier.
+    // Software pipeline over 32-wide contraction slices: the fragments of the next slice are read
+    // from LDS while the MFMAs of the current one run (B fragments into the other of two
+    // register sets, A fragment mf right after its last MFMA of the current slice), so the MFMA
+    // pipe never waits for a fresh read. The barrier that hands a step's slot back sits before
+    // the MFMAs of the step's last slice, whose fragments are already in registers.
+    constexpr int NS = DK / 32;  // slices per step (even)
+    // k order inside a step. bf16: slice h, lane L holds k = 32h + 8(L/16) .. +7 (16-byte chunk
+    // 4h + L/16 of the A and B rows). fp8: a B chunk of 16 bytes holds 16 k, so a lane reads
+    // chunk 4j + L/16 of its B row once for the slice pair (2j, 2j+1), its bytes 0-7 in slice 2j
+    // and 8-15 in slice 2j+1, and A follows the same k (bf16 chunks 8j + 2(L/16) + {0, 1}). Any
+    // k order is the same contraction as long as A and B agree.
+    auto read_a = [&](const u32x4* slot, int h, int mf, bf16x8& dst) __attribute__((always_inline)) {
+      const int c = F8 ? (h >> 1) * 8 + (lane >> 4) * 2 + (h & 1) : h * 4 + (lane >> 4);
+      const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
+      __builtin_memcpy(&dst, &v, 16);
+    };
+    // B chunk of 16-row fragment nf: bf16, the chunk of slice h; fp8, the chunk of slice pair h/2
+    auto read_b = [&](const u32x4* slot, int h, int nf, u32x4& dst) __attribute__((always_inline)) {
+      const int c = F8 ? (h >> 1) * 4 + (lane >> 4) : h * 4 + (lane >> 4);
+      dst = slot[ACH + dswz<CPRB>(wn * WN + nf * 16 + (lane & 15), c)];
+    };
+    auto bar = [&]() __attribute__((always_inline)) {
+      // A bare s_barrier: a fence here would make the compiler drain all outstanding
+      // direct-to-LDS loads. The signal fences only stop the compiler from moving LDS accesses
+      // across the barrier.
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const u32x4* slot = ring + (st % RING) * STAGE;
+    };
+    bf16x8 afr[MF];
+    // B chunks: bf16, those of the current slice and of the next; fp8, one set (a slice pair's)
+    u32x4 bq[F8 ? 1 : 2][NF];
+    // the whole ring is free (the previous item ended with a barrier after its last reads)
 #pragma unroll
-      for (int h = 0; h < DK / 32; ++h) {  // 32-wide MFMA contraction slices of the step
-        const int c = h * 4 + (lane >> 4);
-        bf16x8 bfr[NF], afr[MF];
+    for (int r = 0; r < RING; ++r)
+      if (st_lo + r < st_hi) issue(st_lo + r);
+    // this wave's loads of the first step are done once at most the later steps' are pending
+    wait_vmcnt_dyn<(RING - 1) * LPW>(min(RING - 1, st_hi - 1 - st_lo) * lpw);
+    bar();
+    {
+      const u32x4* slot = ring + (st_lo % RING) * STAGE;
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) read_b(slot, 0, nf, bq[0][nf]);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+        if (!(ASKIP && wm * WM + mf * 16 >= nrows)) read_a(slot, 0, mf, afr[mf]);
+    }
+    for (int st = st_lo; st < st_hi; ++st) {
+      const u32x4* slot = ring + (st % RING) * STAGE;
+      const u32x4* nslot = ring + ((st + 1) % RING) * STAGE;
+      static_for<NS>([&](auto hc) __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        constexpr int P = h & 1;  // B register set of this slice (bf16)
+        // The next slice is read whether or not it exists: past the item's last step the reads
+        // land in registers that are never used (in-bounds LDS, no loads in flight), which keeps
+        // the code free of branches and the compiler's read counts exact.
+        if (h == NS - 1) {
+          wait_lgkmcnt0();  // this wave's reads of step st are back
+          if (st + 1 < st_hi) {
+            // the next slice opens step st+1: this wave's loads of it have landed (at most the
+            // later steps' are pending), and after the barrier both hold for every wave, so
+            // step st's slot takes step st+RING
+            wait_vmcnt_dyn<(RING - 2) * LPW>(min(RING - 2, st_hi - 2 - st) * lpw);
+            bar();
+            if (st + RING < st_hi) issue(st + RING);
+          }
+        }
+        const u32x4* rs = h + 1 < NS ? slot : nslot;
+        const int rh = (h + 1) % NS;
+        bf16x8 bfr[NF];
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
-          const int row = wn * WN + nf * 16 + (lane & 15);
           if constexpr (F8) {
-            // 8 fp8 of k = h*32 + (lane/16)*8: half of chunk c/2 of the 64-byte row
-            const uint2* half = reinterpret_cast<const uint2*>(slot + ACH + dswz<CPRB>(row, c >> 1));
-            bfr[nf] = fp8x8_to_bf16(half[c & 1]);
+            const u32x4 v = bq[0][nf];
+            bfr[nf] = fp8x8_to_bf16((h & 1) ? make_uint2(v[2], v[3]) : make_uint2(v[0], v[1]));
           } else {
-            const u32x4 v = slot[ACH + dswz<CPRB>(row, c)];
-            __builtin_memcpy(&bfr[nf], &v, 16);
+            __builtin_memcpy(&bfr[nf], &bq[P][nf], 16);
           }
+        }
+        // next B chunks: bf16 every slice (into the other set); fp8 after the second slice of a
+        // pair has been widened (into the same set)
+        constexpr int NBR = F8 ? ((h & 1) ? NF : 0) : NF;
+        if constexpr (NBR > 0) {
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) read_b(rs, rh, nf, bq[F8 ? 0 : P ^ 1][nf]);
         }
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) {
           if (ASKIP && wm * WM + mf * 16 >= nrows) continue;  // wave-uniform: absent rows
-          const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
-          __builtin_memcpy(&afr[mf], &v, 16);
-        }
-        // the next loads go out after this slice's fragment reads: DMA writes landing in LDS
-        // while the reads are in progress slow both down
-        if (h == 0 && st + RING - 1 < st_hi) issue(st + RING - 1);
-        // one slice's fragments live at a time: the compiler may not hoist the next slice's
-        // reads above these MFMAs (that would need registers the big tile does not have)
-        if (DK / 32 > 1) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
-            if (ASKIP && wm * WM + mf * 16 >= nrows) continue;  // no MFMA work on absent rows
             if constexpr (F8)
               part[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], part[mf][nf], 0, 0, 0);
             else
               acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
           }
-        if (DK / 32 > 1) __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (F8) {
-        if ((st + 1) % KBS == 0) {  // end of a 128-long scale block
-          const int kb = st / KBS;
-          const float s0 = sc_lds[(wn * 2) * KBn + kb];
-          const float s1 = GATED ? sc_lds[(wn * 2 + 1) * KBn + kb] : s0;
-#pragma unroll
-          for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-            for (int nf = 0; nf < NF; ++nf) {
-              const float sc = (GATED && nf >= NF / 2) ? s1 : s0;
-              acc[mf][nf] += sc * part[mf][nf];
-              part[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+          read_a(rs, rh, mf, afr[mf]);
         }
-      }
+        // instruction order of the slice: the B reads, then per 16-row fragment its MFMAs and
+        // the read of its next A fragment
+        if constexpr (NBR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NBR, 0);
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // the reads stay in this slice (not sunk to their first use)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (F8) {
+          if (h == NS - 1 && (st + 1) % KBS == 0) {  // end of a 128-long scale block
+            const int kb = st / KBS;
+            const float s0 = sc_lds[(wn * 2) * KBn + kb];
+            const float s1 = GATED ? sc_lds[(wn * 2 + 1) * KBn + kb] : s0;
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+              for (int nf = 0; nf < NF; ++nf) {
+                const float sc = (GATED && nf >= NF / 2) ? s1 : s0;
+                acc[mf][nf] += sc * part[mf][nf];
+                part[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+          }
+        }
+      });
     }
     __syncthreads();  // all waves done reading the ring before the next item refills it
     if (MODE == 1 || (MODE == 3 && split)) {

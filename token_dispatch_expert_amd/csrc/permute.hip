@@ -16,13 +16,14 @@
 // deterministic (smaller batches use one workgroup for the first three, see
 // permute_small_kernel):
 //   hist : one workgroup per tile of kPermuteTile flat entries; LDS histogram -> ws[tile][e]
-//   scan : one workgroup; per expert an exclusive prefix over tiles (groups of threads take
-//          ranges of tiles), then counts, the exclusive scan over experts (offsets) and
-//          per-tile bases ws[tile][e]
-//   rank : one wavefront per tile walks its entries in flat order, 64 at a time; lanes with
-//          the same expert find each other with ballots over the expert id's bits, so a
-//          lane's rank among equal keys is a popcount of lower lanes; the group's last lane
-//          advances the running base in LDS. Writes both index maps.
+//   scan : one workgroup per kScanExperts experts; per expert an exclusive prefix over the
+//          tiles (groups of threads take ranges of tiles) -> ws[tile][e], relative to the
+//          expert's first row, and the kept count -> counts[e]
+//   rank : one wavefront per tile; it first scans the kept counts over the experts (offsets;
+//          the first tile's wavefront also stores them), then walks its entries in flat order,
+//          64 at a time; lanes with the same expert find each other with ballots over the
+//          expert id's bits, so a lane's rank among equal keys is a popcount of lower lanes;
+//          the group's last lane advances the running base in LDS. Writes both index maps.
 //   copy : one workgroup per token reads x[t] once in 16-byte vectors and stores it to its
 //          k sorted rows.
 #include "moe_internal.h"
@@ -86,22 +87,24 @@ __device__ __forceinline__ int block_inclusive_scan_1024(int v, int32_t* wave_su
   return v + (wave > 0 ? wave_sum[wave - 1] : 0);
 }
 
-// The 1024 threads are G groups of E (G = 1024 / E, at most the tile count); group g takes a
-// contiguous range of tiles, so thread (g, e) scans at most kScanRegTiles tile counts of expert
-// e in registers (all loaded at once). Group totals give each group's base per expert; the
-// expert totals, capped, are scanned over the experts for the offsets.
-__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ ws,
-                                                                    int n_tiles, int E, int cap,
-                                                                    int32_t* __restrict__ counts,
-                                                                    int32_t* __restrict__ offsets) {
-  __shared__ int32_t gsum[kScanThreads];  // [G][E] group totals
-  __shared__ int32_t expert_off[kScanThreads];
-  __shared__ int32_t wave_sum[kScanThreads / kWave];
+// Workgroup b takes experts b*kScanExperts .. +kScanExperts-1; its threads are kScanGroups
+// groups of kScanExperts, and group g takes a contiguous range of tiles, so thread (g, e) scans
+// at most kScanRegTiles tile counts of expert e in registers (all loaded at once). Group totals
+// give each group's base; the expert's total, capped, is its kept count. The scan over the
+// experts (offsets) is left to the rank kernel, so no single workgroup reads every tile.
+constexpr int kScanExperts = 16;
+constexpr int kScanGroups = 16;
+constexpr int kScanWgThreads = kScanExperts * kScanGroups;
+__global__ __launch_bounds__(kScanWgThreads) void permute_scan_kernel(int32_t* __restrict__ ws,
+                                                                      int n_tiles, int E, int cap,
+                                                                      int32_t* __restrict__ counts,
+                                                                      int32_t* __restrict__ offsets) {
+  __shared__ int32_t gsum[kScanWgThreads];  // [group][expert] group totals
   const int tid = threadIdx.x;
-  const int G = max(1, min(kScanThreads / E, n_tiles));
-  const int g = tid / E, e = tid - g * E;
-  const bool active = g < G;
-  const int tpg = (n_tiles + G - 1) / G;
+  const int g = tid / kScanExperts, el = tid - g * kScanExperts;
+  const int e = blockIdx.x * kScanExperts + el;
+  const bool active = e < E;
+  const int tpg = (n_tiles + kScanGroups - 1) / kScanGroups;
   const int t0 = min(g * tpg, n_tiles), t1 = min(t0 + tpg, n_tiles);
   const bool in_regs = tpg <= kScanRegTiles;
   int pre[kScanRegTiles];
@@ -131,35 +134,30 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
         }
       }
     }
-    gsum[tid] = run;
   }
+  gsum[tid] = run;
   __syncthreads();
   int gbase = 0, total = 0;
-  if (active) {
-    for (int gg = 0; gg < G; ++gg) {
-      const int v = gsum[gg * E + e];
-      gbase += gg < g ? v : 0;
-      total += v;
+#pragma unroll
+  for (int gg = 0; gg < kScanGroups; ++gg) {
+    const int v = gsum[gg * kScanExperts + el];
+    gbase += gg < g ? v : 0;
+    total += v;
+  }
+  if (active && g == 0) {
+    counts[e] = min(total, cap);  // kept assignments (capacity factor)
+    if (n_tiles == 0) {           // no rank launch follows: the offsets of an empty batch
+      offsets[e] = 0;
+      if (e == 0) offsets[E] = 0;
     }
   }
-  // threads 0..E-1 are group 0: one per expert
-  const int kept = tid < E ? min(total, cap) : 0;  // kept assignments (capacity factor)
-  const int incl = block_inclusive_scan_1024(kept, wave_sum);
-  if (tid < E) {
-    counts[tid] = kept;
-    offsets[tid] = incl - kept;
-    expert_off[tid] = incl - kept;
-  }
-  if (tid == kScanThreads - 1) offsets[E] = incl;
-  __syncthreads();
   if (active) {
-    const int base = expert_off[e] + gbase;
     if (in_regs) {
 #pragma unroll
       for (int u = 0; u < kScanRegTiles; ++u)
-        if (t0 + u < t1) ws[(size_t)(t0 + u) * E + e] = pre[u] + base;
+        if (t0 + u < t1) ws[(size_t)(t0 + u) * E + e] = pre[u] + gbase;
     } else {
-      for (int t = t0; t < t1; ++t) ws[(size_t)t * E + e] += base;
+      for (int t = t0; t < t1; ++t) ws[(size_t)t * E + e] += gbase;
     }
   }
 }
@@ -167,7 +165,8 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
 __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __restrict__ ids,
                                                              int R, int E, int nbits,
                                                              const int32_t* __restrict__ ws,
-                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ s2f,
                                                              int32_t* __restrict__ f2s) {
   extern __shared__ int32_t run[];  // [E] running positions, then [E] end of each expert
@@ -175,14 +174,37 @@ __global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __re
   const int lane = threadIdx.x;
   const int32_t* bases = ws + (size_t)blockIdx.x * E;
   for (int e = lane; e < E; e += kWave) {
-    run[e] = bases[e];
-    lim[e] = offsets[e + 1];
+    run[e] = bases[e];  // relative to the expert's first row
+    lim[e] = counts[e];
   }
   // One wavefront per workgroup: its LDS accesses take effect in program order, so no barrier
-  // is needed between the writes above and the reads below, nor between a chunk's reads of the
-  // running positions and their update (a workgroup barrier would also wait for this wave's
-  // global stores of the index maps, once per chunk). The wave barriers only keep the compiler
-  // from moving LDS accesses across them.
+  // is needed between LDS writes and later reads, nor between a chunk's reads of the running
+  // positions and their update (a workgroup barrier would also wait for this wave's global
+  // stores of the index maps, once per chunk). The wave barriers only keep the compiler from
+  // moving LDS accesses across them.
+  __builtin_amdgcn_wave_barrier();
+  // offsets: exclusive scan of the kept counts, lane l taking experts l*epl .. +epl-1
+  {
+    const int epl = (E + kWave - 1) / kWave;
+    const int e0 = min(lane * epl, E), e1 = min(e0 + epl, E);
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += lim[e];
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    int o = incl - sum;
+    for (int e = e0; e < e1; ++e) {
+      const int c = lim[e];
+      if (blockIdx.x == 0) offsets[e] = o;
+      run[e] += o;
+      lim[e] = o + c;  // positions at or past it are beyond the capacity
+      o += c;
+    }
+    if (blockIdx.x == 0 && lane == kWave - 1) offsets[E] = incl;
+  }
   __builtin_amdgcn_wave_barrier();
   const int base = blockIdx.x * kPermuteTile;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -359,10 +381,11 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
   }
-  permute_scan_kernel<<<1, kScanThreads, 0, stream>>>(ws, n_tiles, E, cap, counts, offsets);
+  permute_scan_kernel<<<(E + kScanExperts - 1) / kScanExperts, kScanWgThreads, 0, stream>>>(
+      ws, n_tiles, E, cap, counts, offsets);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess || n_tiles == 0) return st;
-  permute_rank_kernel<<<n_tiles, kWave, 2 * lds, stream>>>(ids, R, E, nbits, ws, offsets,
+  permute_rank_kernel<<<n_tiles, kWave, 2 * lds, stream>>>(ids, R, E, nbits, ws, counts, offsets,
                                                             sorted_to_flat, flat_to_sorted);
   st = hipGetLastError();
   if (st != hipSuccess) return st;

@@ -96,6 +96,37 @@ def test_permute_capacity_prefill_size(dev):
         assert np.array_equal(out["sorted_to_flat"][:kept].cpu().numpy(), ref["sorted_to_flat"])
 
 
+@pytest.mark.parametrize("T,E,k,cap_pct", [
+    (9000, 1, 1, None),     # one expert
+    (1000, 17, 9, None),    # the last 16-expert scan workgroup holds one expert
+    (600, 1024, 16, None),  # the expert limit: every rank wavefront scans 16 counts per lane
+    (40000, 33, 8, None),   # 1,250 tiles: more than the scan keeps in registers
+    (3000, 300, 4, 110),    # capacity on a partial scan workgroup
+])
+def test_permute_large_batches(dev, T, E, k, cap_pct):
+    """The multi-launch permutation (more than 8192 assignments) at expert counts and tile
+    counts the prefill workloads do not reach: counts, offsets, both maps and the sorted rows
+    bit for bit against the oracle's stable counting sort."""
+    rng = np.random.default_rng(T * 31 + E)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)  # k distinct experts
+    x = rng.integers(-32768, 32768, size=(T, 8), dtype=np.int16)          # bf16 bit patterns
+    cap = None if cap_pct is None else moe.moe_expert_capacity(T, E, k, cap_pct)
+    ref = oracle.permute(ids, E, cap)
+    xd = torch.from_numpy(x).to(dev).view(torch.bfloat16)
+    out = layer_buffers(T, E, k, 8, torch.bfloat16, device=dev)
+    ws = moe.Workspace(moe.moe_permute_workspace_size(T, E, k), device=dev)
+    kw = {} if cap is None else {"capacity": cap}
+    moe.moe_permute(xd, torch.from_numpy(ids).to(dev), E, out["counts"], out["offsets"],
+                    out["sorted_to_flat"], out["flat_to_sorted"], out["x_sorted"], ws, **kw)
+    torch.cuda.synchronize()
+    kept = int(ref["offsets"][-1])
+    for n in ("counts", "offsets", "flat_to_sorted"):
+        assert np.array_equal(out[n].cpu().numpy(), ref[n]), n
+    assert np.array_equal(out["sorted_to_flat"][:kept].cpu().numpy(), ref["sorted_to_flat"])
+    xs = out["x_sorted"][:kept].view(torch.int16).cpu().numpy()
+    assert np.array_equal(xs, x[ref["sorted_to_flat"] // k])
+
+
 def test_combine_skips_dropped_slots(dev):
     rng = np.random.default_rng(5)
     T, k, d = 37, 3, 64

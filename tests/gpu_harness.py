@@ -97,6 +97,12 @@ def run_layer(cfg: synth.Config, logits: np.ndarray, x: np.ndarray, W: DeviceWei
     out = layer_buffers(cfg.T, cfg.E, cfg.k, cfg.d, ACT_TORCH[cfg.act], device=dev)
     ws = moe.Workspace(moe.moe_layer_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff,
                                                     ACT_TORCH[cfg.act], W_TORCH[cfg.w]), device=dev)
+    # poison every output and the workspace: fresh allocations often reuse the blocks of the
+    # previous run, whose values an unwritten output would otherwise inherit (and a repeat
+    # comparison would then pass); the library must not rely on a cleared workspace either
+    for t in out.values():
+        t.fill_(float("nan")) if t.is_floating_point() else t.fill_(-7)
+    ws.buf.fill_(0xFF)
     moe.moe_layer(lg, xd, W.gate, W.up, W.down, cfg.k, out, ws, **W.kwargs())
     torch.cuda.synchronize()
     return {n: to_host(t) for n, t in out.items()}

@@ -42,6 +42,7 @@ def check_capped(cfg, got, ref, cap):
     assert int(got["offsets"][-1]) == kept
     for n in ("topk_ids", "counts", "offsets", "flat_to_sorted"):
         assert np.array_equal(got[n], ref[n]), n
+    H.check_gates(got["topk_gates"], ref["topk_gates"], cfg.k)
     assert np.array_equal(got["sorted_to_flat"][:kept], ref["sorted_to_flat"]), "sorted_to_flat"
     assert np.array_equal(got["x_sorted"][:kept], ref["x_sorted"]), "x_sorted"
     tol = H.TOL[cfg.w]
@@ -59,6 +60,7 @@ def check_capped(cfg, got, ref, cap):
 
 
 @pytest.mark.parametrize("T,E,k,d,d_ff,act,w", [
+    (100, 300, 6, 256, 256, "bf16", "bf16"),   # many experts (5 per lane in the route)
     (300, 16, 4, 256, 256, "bf16", "bf16"),    # single-workgroup permutation
     (3000, 64, 4, 128, 128, "f32", "f32"),     # T*k = 12000: tiled permutation
 ])

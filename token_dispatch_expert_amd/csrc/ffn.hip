@@ -1151,6 +1151,10 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
             if (st + RING < st_hi) issue(st + RING);
           }
         }
+        // fp8: the wave issuing a slice's conversions, MFMAs and reads runs at raised priority, so
+        // the SIMD's other wave, in its barrier or load issue, does not hold it back (c5 FFN -2%;
+        // bf16 tiles measured 0.5% slower with it)
+        if constexpr (F8) __builtin_amdgcn_s_setprio(1);
         const u32x4* rs = h + 1 < NS ? slot : nslot;
         const int rh = (h + 1) % NS;
         bf16x8 bfr[NF];
@@ -1192,6 +1196,7 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
         }
         // the reads stay in this slice (not sunk to their first use)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (F8) __builtin_amdgcn_s_setprio(0);
         if constexpr (F8) {
           if (h == NS - 1 && (st + 1) % KBS == 0) {  // end of a 128-long scale block
             const int kb = st / KBS;

@@ -362,6 +362,25 @@ def check_router_logits():
     assert np.array_equal(got, oracle.decode_bf16(xb)[:, cols])
 
 
+def check_rel_max_err():
+    # the error measure the tolerances are stated in: max|got - ref| / sqrt(mean(ref^2)),
+    # worked by hand on inputs where max and mean error, and rms and max|ref|, all differ
+    f = oracle.rel_max_err
+    assert math.isclose(f(np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.0, 4.0])), 1.0 / math.sqrt(7.0),
+                        rel_tol=1e-15)
+    assert math.isclose(f(np.array([0.0, 0.0, 3.0]), np.array([1.0, 1.0, 1.0])), 2.0, rel_tol=1e-15)
+    # rms(ref) = sqrt((9 + 16) / 2) = 5 / sqrt(2); max|ref| = 4; the error is below the reference
+    assert math.isclose(f(np.array([3.0, 3.0]), np.array([3.0, 4.0])), math.sqrt(2.0) / 5.0, rel_tol=1e-15)
+    # 2-D inputs are measured over all elements; rms = sqrt(30 / 4), max|err| = 0.5
+    got = np.array([[1.0, -2.0], [3.5, 4.0]])
+    ref = np.array([[1.0, -2.0], [3.0, 4.0]])
+    assert math.isclose(f(got, ref), 0.5 / math.sqrt(7.5), rel_tol=1e-15)
+    # scale invariance, exact zero, and the all-zero reference (absolute error)
+    assert math.isclose(f(8.0 * got, 8.0 * ref), f(got, ref), rel_tol=1e-15)
+    assert f(ref, ref) == 0.0
+    assert f(np.array([0.5, -2.0]), np.zeros(2)) == 2.0
+
+
 CHECKS = [
     check_decode_bf16, check_decode_e4m3fn, check_route_vs_stable_argsort,
     check_route_special_cases, check_permute_vs_library, check_golden_load_example,
@@ -369,6 +388,7 @@ CHECKS = [
     check_identity_experts_and_gather, check_fp8_dequant_blocks, check_bf16_layer_decodes_inputs,
     check_bf16_value_rounding, check_capacity_formula, check_capacity_golden_example,
     check_capacity_vs_library, check_capacity_brute_force_layer, check_router_logits,
+    check_rel_max_err,
 ]
 
 
@@ -381,7 +401,7 @@ def test_oracle_pin(check):
 # the pins must catch plausible mistakes planted in the oracle
 # ----------------------------------------------------------------------------------------
 _ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16",
-                                     "expert_capacity", "router_logits")}
+                                     "expert_capacity", "router_logits", "rel_max_err")}
 
 
 def _mut_route_tie_high(logits, k):
@@ -522,6 +542,28 @@ def _mut_router_untransposed_rows(x, x_fmt, w_router, w_fmt):
     return X @ Wr[::-1].T
 
 
+def _mut_err_mean(got, ref):
+    # mean |error| in place of the largest
+    ref, got = np.asarray(ref, np.float64), np.asarray(got, np.float64)
+    return float(np.mean(np.abs(got - ref))) / float(np.sqrt(np.mean(ref * ref)))
+
+
+def _mut_err_max_ref(got, ref):
+    # the largest |ref| in place of the rms
+    ref, got = np.asarray(ref, np.float64), np.asarray(got, np.float64)
+    return float(np.max(np.abs(got - ref))) / float(np.max(np.abs(ref)))
+
+
+def _mut_err_no_sqrt(got, ref):
+    ref, got = np.asarray(ref, np.float64), np.asarray(got, np.float64)
+    return float(np.max(np.abs(got - ref))) / float(np.mean(ref * ref))
+
+
+def _mut_err_mean_abs_ref(got, ref):
+    ref, got = np.asarray(ref, np.float64), np.asarray(got, np.float64)
+    return float(np.max(np.abs(got - ref))) / float(np.mean(np.abs(ref)))
+
+
 MUTANTS = {
     "route_tie_high": ("route", _mut_route_tie_high),
     "route_full_softmax": ("route", _mut_route_full_softmax),
@@ -542,6 +584,10 @@ MUTANTS = {
     "combine_wrong_map": ("combine", _mut_combine_wrong_map),
     "decode_bf16_shift": ("decode_bf16", _mut_decode_bf16_shift),
     "decode_e4m3_bias8": ("decode_e4m3fn", _mut_decode_e4m3_bias8),
+    "rel_err_mean": ("rel_max_err", _mut_err_mean),
+    "rel_err_max_ref": ("rel_max_err", _mut_err_max_ref),
+    "rel_err_no_sqrt": ("rel_max_err", _mut_err_no_sqrt),
+    "rel_err_mean_abs_ref": ("rel_max_err", _mut_err_mean_abs_ref),
 }
 
 

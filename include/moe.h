@@ -207,10 +207,14 @@ moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const 
  *   assignment dropped by moe_permute_capped) adds nothing; so does one at or past T*k.
  *
  *   y_sorted [T*k, d] fp32; flat_to_sorted [T*k] int32; topk_gates [T, k] fp32;
- *   y [T, d] fp32 out. Requires d a multiple of 4.
+ *   y [T, d] out, in y_dtype: MOE_F32 (the fp32 sum itself) or MOE_BF16 (that fp32 sum rounded
+ *   to the nearest bf16, ties to even: half the bytes written, and a final rounding of up to
+ *   2^-9 of each value). MOE_FP8_E4M3FN gives MOE_ERR_UNSUPPORTED, any other value
+ *   MOE_ERR_INVALID_ARG. Requires d a multiple of 4 and y 16-byte aligned.
  */
 moe_status_t moe_combine(const float* y_sorted, const int32_t* flat_to_sorted,
-                         const float* topk_gates, int T, int k, int d, float* y, void* stream);
+                         const float* topk_gates, int T, int k, int d, void* y,
+                         moe_dtype_t y_dtype, void* stream);
 
 /* Bytes of workspace moe_layer needs. */
 size_t moe_layer_workspace_size(int T, int E, int k, int d, int d_ff, moe_dtype_t act_dtype,
@@ -219,7 +223,8 @@ size_t moe_layer_workspace_size(int T, int E, int k, int d, int d_ff, moe_dtype_
 /*
  * moe_layer - the whole layer on one stream: moe_route, moe_permute, moe_grouped_ffn and
  * moe_combine in order, with every intermediate written to a caller buffer so that each can
- * be checked. Arguments have the meanings given above; x and x_sorted are in act_dtype.
+ * be checked. Arguments have the meanings given above; x and x_sorted are in act_dtype, y in
+ * y_dtype (as moe_combine).
  */
 moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype, int T, int E,
                        int k, int d, int d_ff, const void* w_gate, const void* w_up,
@@ -227,8 +232,8 @@ moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype
                        const float* s_up, const float* s_down, int32_t* topk_ids,
                        float* topk_gates, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
-                       float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       float* y_sorted, void* y, moe_dtype_t y_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * moe_layer_capped - moe_layer with moe_permute_capped in place of moe_permute (each expert
@@ -241,8 +246,8 @@ moe_status_t moe_layer_capped(const float* logits, const void* x, moe_dtype_t ac
                               const float* s_gate, const float* s_up, const float* s_down,
                               int32_t* topk_ids, float* topk_gates, int32_t* counts,
                               int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
-                              void* x_sorted, float* y_sorted, float* y, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              void* x_sorted, float* y_sorted, void* y, moe_dtype_t y_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

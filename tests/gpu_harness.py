@@ -127,3 +127,50 @@ def check_gates(got_gates: np.ndarray, ref_gates: np.ndarray, k: int):
 
 def active_experts(ref_counts: np.ndarray):
     return [int(e) for e in np.nonzero(ref_counts)[0]]
+
+
+def covering_tokens(cfg, perm, n_random, seed=0, block=128, small=16):
+    """Tokens whose rows reach every kernel role and every output tile of the full-size layer:
+    n_random seeded tokens, plus the owners of every expert's first and last sorted row, of the
+    first row of each of its 128-row blocks (so every row tile of 128 or 256 rows, the
+    last-round split tiles included, holds a checked row; a y_sorted row spans every column
+    tile of both GEMMs) and of every row of the experts with at most `small` rows (the
+    streaming role's 16-row tiles)."""
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(cfg.T, size=n_random, replace=False).tolist())
+    off, s2f = perm["offsets"], perm["sorted_to_flat"]
+    for e in range(cfg.E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b == a:
+            continue
+        rows = range(a, b) if b - a <= small else list(range(a, b, block)) + [b - 1]
+        toks.update(int(s2f[r]) // cfg.k for r in rows)
+    return sorted(toks)
+
+
+def sampled_reference(toks, ids, gates, x, cfg, W, h_rounds=(None, "bf16")):
+    """The oracle's y rows and per-slot expert outputs for the listed tokens, for each h
+    rounding in h_rounds, decoding every expert's weights once (oracle.layer_tokens per
+    rounding would decode them twice). Returns {h_round: (y [len(toks), d], {(t, j): row})}."""
+    k = cfg.k
+    X = oracle.decode_activations(np.asarray(x)[toks], cfg.act)
+    by_expert = {}
+    for ti, t in enumerate(toks):
+        for j in range(k):
+            by_expert.setdefault(int(ids[t, j]), []).append((ti, j))
+    dec = oracle.make_weight_decoder(W.raw, cfg.w)
+    out = {}
+    ys = {hr: np.zeros((len(toks) * k, cfg.d)) for hr in h_rounds}
+    for e, items in sorted(by_expert.items()):
+        Wg, Wu, Wd = dec(e)
+        Xe = X[[ti for ti, _ in items]]
+        for hr in h_rounds:
+            Y = oracle.expert_ffn(Xe, Wg, Wu, Wd, h_round=hr)
+            for (ti, j), yr in zip(items, Y):
+                ys[hr][ti * k + j] = yr
+    f2s = np.arange(len(toks) * k, dtype=np.int32)
+    for hr in h_rounds:
+        y = oracle.combine(ys[hr], f2s, np.asarray(gates)[toks])
+        rows = {(t, j): ys[hr][ti * k + j] for ti, t in enumerate(toks) for j in range(k)}
+        out[hr] = (y, rows)
+    return out

@@ -105,7 +105,7 @@ def test_capacity_entry_points(lib):
     d_ff = 256
     need = lib.moe_layer_workspace_size(T, E, k, d, d_ff, B.MOE_BF16, B.MOE_BF16)
     la = [P, P2, B.MOE_BF16, T, E, k, d, d_ff, -3, P, P2, P3, B.MOE_BF16, None, None, None,
-          P, P2, P3, P, P2, P3, P, P2, P3, P, need, None]
+          P, P2, P3, P, P2, P3, P, P2, P3, B.MOE_F32, P, need, None]
     assert lib.moe_layer_capped(*la) == B.MOE_ERR_INVALID_ARG
     la[8], la[-2] = 4, need - 16
     assert lib.moe_layer_capped(*la) == B.MOE_ERR_WORKSPACE
@@ -141,16 +141,22 @@ def test_ffn_rejects_bad_arguments(lib):
 
 def test_combine_and_layer_reject_bad_arguments(lib):
     c = lib.moe_combine
-    assert c(P, P2, P3, 4, 2, 6, P, None) == B.MOE_ERR_UNSUPPORTED   # d not /4
-    assert c(None, P2, P3, 4, 2, 8, P, None) == B.MOE_ERR_INVALID_ARG
-    assert c(P, P2, P3, 4, 0, 8, P, None) == B.MOE_ERR_INVALID_ARG
+    assert c(P, P2, P3, 4, 2, 6, P, B.MOE_F32, None) == B.MOE_ERR_UNSUPPORTED   # d not /4
+    assert c(None, P2, P3, 4, 2, 8, P, B.MOE_F32, None) == B.MOE_ERR_INVALID_ARG
+    assert c(P, P2, P3, 4, 0, 8, P, B.MOE_F32, None) == B.MOE_ERR_INVALID_ARG
+    assert c(P, P2, P3, 4, 2, 8, P, B.MOE_FP8_E4M3FN, None) == B.MOE_ERR_UNSUPPORTED  # fp8 output
+    assert c(P, P2, P3, 4, 2, 8, P, 7, None) == B.MOE_ERR_INVALID_ARG                 # no such format
+    assert c(P, P2, P3, 4, 2, 8, MIS, B.MOE_BF16, None) == B.MOE_ERR_INVALID_ARG      # y misaligned
     T, E, k, d, d_ff = 16, 8, 2, 128, 256
     need = lib.moe_layer_workspace_size(T, E, k, d, d_ff, B.MOE_BF16, B.MOE_BF16)
     assert need == lib.moe_permute_workspace_size(T, E, k) + lib.moe_ffn_workspace_size(T * k, E, d, d_ff, B.MOE_BF16, B.MOE_BF16)
     args = [P, P2, B.MOE_BF16, T, E, k, d, d_ff, P, P2, P3, B.MOE_BF16, None, None, None,
-            P, P2, P3, P, P2, P3, P, P2, P3, P, need - 16, None]
+            P, P2, P3, P, P2, P3, P, P2, P3, B.MOE_F32, P, need - 16, None]
     assert lib.moe_layer(*args) == B.MOE_ERR_WORKSPACE
     args[-2] = need
+    args[-4] = 9
+    assert lib.moe_layer(*args) == B.MOE_ERR_INVALID_ARG     # no such output format
+    args[-4] = B.MOE_BF16
     args[2] = B.MOE_FP8_E4M3FN
     assert lib.moe_layer(*args) == B.MOE_ERR_UNSUPPORTED
 

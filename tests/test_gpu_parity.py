@@ -26,8 +26,9 @@ def dev():
     return H.require_gpu()
 
 
-def run_full(cfg, dev, logits=None, x=None):
-    """Whole layer vs the whole oracle."""
+def run_full(cfg, dev, logits=None, x=None, plain_bar=True):
+    """Whole layer vs the whole oracle. plain_bar=False keeps the plain fp64 comparison as a
+    printed figure only (see the narrow-width case) and asserts the rounding-point bar."""
     lg0, x0 = synth.make_routing_inputs(cfg)
     logits = lg0 if logits is None else logits
     x = x0 if x is None else x
@@ -42,7 +43,10 @@ def run_full(cfg, dev, logits=None, x=None):
     e_ys = oracle.rel_max_err(got["y_sorted"], ref["y_sorted"])
     e_y = oracle.rel_max_err(got["y"], ref["y"])
     print(f"{cfg.name}: y_sorted err {e_ys:.3e}, y err {e_y:.3e} (tol {tol})", flush=True)
-    assert e_ys <= tol and e_y <= tol
+    if plain_bar:
+        assert e_ys <= tol and e_y <= tol
+    else:
+        assert cfg.act == "bf16", "only the bf16 rounding point replaces the plain bar"
     if cfg.act == "bf16":
         refh = oracle.layer(logits, x, cfg.act, W.raw, cfg.w, cfg.k, h_round="bf16")
         e_ys2 = oracle.rel_max_err(got["y_sorted"], refh["y_sorted"])
@@ -54,29 +58,36 @@ def run_full(cfg, dev, logits=None, x=None):
 
 
 def run_sampled(cfg, dev, n_tokens, seed=0):
-    """Full-size layer: routing/permutation in full, float outputs on sampled tokens."""
+    """Full-size layer: routing/permutation in full, float outputs on a token sample that
+    reaches every active expert, every row tile and every kernel role."""
     logits, x = synth.make_routing_inputs(cfg)
     ref_ids, ref_gates = oracle.route(logits, cfg.k)
     perm = oracle.permute(ref_ids, cfg.E)
     W = H.DeviceWeights(cfg, dev, experts=H.active_experts(perm["counts"]))
+    print(f"{cfg.name}: weights on the device, running the layer", flush=True)
     got = H.run_layer(cfg, logits, x, W, dev)
     H.check_routing_exact(got, dict(topk_ids=ref_ids, **perm), cfg.E)
     H.check_gates(got["topk_gates"], ref_gates, cfg.k)
     xs_ref = oracle.gather_rows(x, perm["sorted_to_flat"], cfg.k)
     assert np.array_equal(got["x_sorted"], xs_ref), "x_sorted bytes differ"
-    toks = sorted(np.random.default_rng(seed).choice(cfg.T, size=n_tokens, replace=False).tolist())
-    y_ref, rows = oracle.layer_tokens(toks, ref_ids, ref_gates, x, cfg.act, W.raw, cfg.w)
+    assert np.all(np.isfinite(got["y"])), "non-finite output (an expert without rows was read?)"
+    toks = H.covering_tokens(cfg, perm, n_tokens, seed)
+    print(f"{cfg.name}: routing exact; oracle on {len(toks)} tokens", flush=True)
+    refs = H.sampled_reference(toks, ref_ids, ref_gates, x, cfg, W)
+    y_ref, rows = refs[None]
+    keys = sorted(rows)
+    ys_got = np.stack([got["y_sorted"][perm["flat_to_sorted"][t * cfg.k + j]] for t, j in keys])
     tol = H.TOL[cfg.w]
     e_y = oracle.rel_max_err(got["y"][toks], y_ref)
-    keys = sorted(rows)
-    ys_ref = np.stack([rows[key] for key in keys])
-    ys_got = np.stack([got["y_sorted"][perm["flat_to_sorted"][t * cfg.k + j]] for t, j in keys])
-    e_ys = oracle.rel_max_err(ys_got, ys_ref)
-    print(f"{cfg.name}: {len(toks)} sampled tokens: y_sorted err {e_ys:.3e}, y err {e_y:.3e} (tol {tol})",
-          flush=True)
-    assert np.all(np.isfinite(got["y"])), "non-finite output (an expert without rows was read?)"
+    e_ys = oracle.rel_max_err(ys_got, np.stack([rows[key] for key in keys]))
+    covered = {int(np.searchsorted(perm["offsets"], perm["flat_to_sorted"][t * cfg.k + j], side="right")) - 1
+               for t, j in keys}
+    active = set(H.active_experts(perm["counts"]))
+    print(f"{cfg.name}: {len(toks)} sampled tokens, {len(keys)} y_sorted rows of {len(covered)}/{len(active)} "
+          f"active experts: y_sorted err {e_ys:.3e}, y err {e_y:.3e} (tol {tol})", flush=True)
+    assert covered == active, "the sample misses an active expert"
     assert e_ys <= tol and e_y <= tol
-    y_ref2, rows2 = oracle.layer_tokens(toks, ref_ids, ref_gates, x, cfg.act, W.raw, cfg.w, h_round="bf16")
+    y_ref2, rows2 = refs["bf16"]
     e_y2 = oracle.rel_max_err(got["y"][toks], y_ref2)
     e_ys2 = oracle.rel_max_err(ys_got, np.stack([rows2[key] for key in keys]))
     print(f"{cfg.name}: vs bf16-h oracle: y_sorted err {e_ys2:.3e}, y err {e_y2:.3e} "
@@ -180,9 +191,49 @@ def test_fp8_small(dev):
 
 
 def test_many_experts_and_topk_limits(dev):
-    # E and k at their limits. (With d_ff = 64 the bf16 rounding of h alone reaches 2.09e-2 of
-    # rms for this seed, over the 2e-2 bound that is stated for the workloads' widths.)
+    # E and k at their limits
     run_full(synth.tiny_config(T=20, d=128, E=1024, k=32, d_ff=256, act="bf16", w="bf16", seed=9), dev)
+
+
+def test_narrow_expert_width(dev):
+    # d_ff = 64: the down GEMM's whole contraction is one 64-wide step of the direct-to-LDS ring.
+    # At this width the bf16 rounding of h alone moves y by 2.09e-2 of its rms for this seed (a
+    # CPU emulation of that rounding point gives the GPU's figure), over the 2e-2 bound stated for
+    # the workloads' widths, so the case is held to the bf16-h oracle's 5e-3 bar instead.
+    cfg = synth.tiny_config(T=20, d=128, E=1024, k=32, d_ff=64, act="bf16", w="bf16", seed=9)
+    assert cfg.T * cfg.k < 32 * cfg.E  # the decode-sized tiles
+    run_full(cfg, dev, plain_bar=False)
+
+
+def test_bf16_output_is_rounded_fp32_sum(dev):
+    # MOE_BF16 output: the fp32 combine result rounded to nearest even, bit for bit (torch's
+    # float32 -> bfloat16 conversion rounds to nearest even), through moe_combine and moe_layer
+    rng = np.random.default_rng(21)
+    T, k, d = 300, 6, 520
+    ys = torch.from_numpy((rng.standard_normal((T * k, d)) * np.exp(rng.uniform(-20, 20, (T * k, 1))))
+                          .astype(np.float32)).to(dev)
+    f2s = torch.from_numpy(rng.permutation(T * k).astype(np.int32)).to(dev)
+    g = torch.from_numpy(rng.dirichlet(np.ones(k), size=T).astype(np.float32)).to(dev)
+    y32 = torch.full((T, d), float("nan"), dtype=torch.float32, device=dev)
+    y16 = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    moe.moe_combine(ys, f2s, g, y32)
+    moe.moe_combine(ys, f2s, g, y16)
+    torch.cuda.synchronize()
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    cfg = synth.tiny_config(T=70, d=256, E=12, k=4, d_ff=384, act="bf16", w="bf16", zipf_s=1.0, seed=22)
+    logits, x = synth.make_routing_inputs(cfg)
+    W = H.DeviceWeights(cfg, dev)
+    outs = {}
+    for ydt in (torch.float32, torch.bfloat16):
+        out = layer_buffers(cfg.T, cfg.E, cfg.k, cfg.d, torch.bfloat16, device=dev, y_dtype=ydt)
+        ws = moe.Workspace(moe.moe_layer_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff,
+                                                        torch.bfloat16, torch.bfloat16), device=dev)
+        out["y"].fill_(float("nan"))
+        moe.moe_layer(torch.from_numpy(logits).to(dev), H.to_dev(x, "bf16", dev), W.gate, W.up, W.down,
+                      cfg.k, out, ws)
+        torch.cuda.synchronize()
+        outs[ydt] = out["y"]
+    assert torch.equal(outs[torch.bfloat16].view(torch.int16), outs[torch.float32].to(torch.bfloat16).view(torch.int16))
 
 
 @pytest.mark.parametrize("E,k", [(12, 3), (300, 7)])

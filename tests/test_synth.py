@@ -78,3 +78,31 @@ def test_layer_tokens_matches_layer():
     assert np.allclose(y, full["y"][toks], rtol=1e-12, atol=1e-12)
     for (t, j), yr in rows.items():
         assert np.allclose(yr, full["y_sorted"][full["flat_to_sorted"][t * cfg.k + j]], rtol=1e-12, atol=1e-12)
+
+
+def test_sampled_reference_matches_layer():
+    # the GPU tests' per-token reference (every expert decoded once, both h roundings) is the
+    # whole oracle's result on those tokens
+    import types
+    import gpu_harness as H
+    cfg = synth.tiny_config(T=40, d=32, E=6, k=3, d_ff=48, act="bf16", w="bf16", zipf_s=1.2, seed=5)
+    logits, x = synth.make_routing_inputs(cfg)
+    Wd = {e: synth.make_expert_weights(cfg, e) for e in range(cfg.E)}
+    W = types.SimpleNamespace(raw=lambda e: Wd[e])
+    ids, gates = oracle.route(logits, cfg.k)
+    perm = oracle.permute(ids, cfg.E)
+    toks = H.covering_tokens(cfg, perm, 3, block=8, small=4)
+    # every expert's first and last row and the first row of each 8-row block are owned by a
+    # sampled token
+    owned = {int(perm["flat_to_sorted"][t * cfg.k + j]) for t in toks for j in range(cfg.k)}
+    for e in range(cfg.E):
+        a, b = int(perm["offsets"][e]), int(perm["offsets"][e + 1])
+        want = set(range(a, b)) if b - a <= 4 else set(range(a, b, 8)) | ({b - 1} if b > a else set())
+        assert want <= owned
+    refs = H.sampled_reference(toks, ids, gates, x, cfg, W)
+    for hr in (None, "bf16"):
+        full = oracle.layer(logits, x, "bf16", W.raw, "bf16", cfg.k, h_round=hr)
+        y, rows = refs[hr]
+        assert np.allclose(y, full["y"][toks], rtol=1e-12, atol=1e-12)
+        for (t, j), yr in rows.items():
+            assert np.allclose(yr, full["y_sorted"][full["flat_to_sorted"][t * cfg.k + j]], rtol=1e-12, atol=1e-12)

@@ -60,16 +60,16 @@ def load_library(path: str | None = None):
         "moe_permute": ([P, I, P, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "moe_ffn_workspace_size": ([I, I, I, I, I, I], S),
         "moe_grouped_ffn": ([P, I, P, I, I, I, I, P, P, P, I, P, P, P, P, P, S, P], I),
-        "moe_combine": ([P, P, P, I, I, I, P, P], I),
+        "moe_combine": ([P, P, P, I, I, I, P, I, P], I),
         "moe_layer_workspace_size": ([I, I, I, I, I, I, I], S),
         "moe_layer": ([P, P, I, I, I, I, I, I, P, P, P, I, P, P, P,
-                       P, P, P, P, P, P, P, P, P, P, S, P], I),
+                       P, P, P, P, P, P, P, P, P, I, P, S, P], I),
         "moe_expert_capacity": ([I, I, I, I], I),
         "moe_route_gemm": ([P, I, P, I, I, I, I, I, P, P, P, P, P, S, P], I),
         "moe_route_gemm_workspace_size": ([I, I, I], S),
         "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
-                              P, P, P, P, P, P, P, P, P, P, S, P], I),
+                              P, P, P, P, P, P, P, P, P, I, P, S, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -242,7 +242,16 @@ def moe_grouped_ffn(x_sorted, offsets, w_gate, w_up, w_down, y_sorted, workspace
         workspace.ptr, workspace.nbytes, _stream(stream)))
 
 
+def _y_dt(y):
+    """The combine's output format, from y's dtype: float32 or bfloat16."""
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"y: expected float32 or bfloat16, got {y.dtype}")
+    return _DTYPE_ENUM[y.dtype]
+
+
 def moe_combine(y_sorted, flat_to_sorted, topk_gates, y, stream=None):
+    """y (float32 or bfloat16) receives the gate-weighted sums; bfloat16 is the fp32 sum
+    rounded to nearest even."""
     T, k = topk_gates.shape
     R, d = y_sorted.shape
     if R != T * k:
@@ -250,16 +259,16 @@ def moe_combine(y_sorted, flat_to_sorted, topk_gates, y, stream=None):
     _need(y_sorted, torch.float32, (R, d), "y_sorted")
     _need(flat_to_sorted, torch.int32, (R,), "flat_to_sorted")
     _need(topk_gates, torch.float32, (T, k), "topk_gates")
-    _need(y, torch.float32, (T, d), "y")
+    _need(y, y.dtype, (T, d), "y")
     _check(load_library().moe_combine(_ptr(y_sorted), _ptr(flat_to_sorted), _ptr(topk_gates), T,
-                                      k, d, _ptr(y), _stream(stream)))
+                                      k, d, _ptr(y), _y_dt(y), _stream(stream)))
 
 
 def moe_layer(logits, x, w_gate, w_up, w_down, k: int, out: dict, workspace: Workspace,
               s_gate=None, s_up=None, s_down=None, stream=None, capacity: int | None = None):
     """out holds the caller's buffers: topk_ids, topk_gates, counts, offsets, sorted_to_flat,
-    flat_to_sorted, x_sorted, y_sorted, y (see `layer_buffers`). capacity (optional): most
-    kept assignments per expert (moe_layer_capped)."""
+    flat_to_sorted, x_sorted, y_sorted, y (see `layer_buffers`; y float32 or bfloat16).
+    capacity (optional): most kept assignments per expert (moe_layer_capped)."""
     T, E = logits.shape
     _need(logits, torch.float32, (T, E), "logits")
     Ew, d, d_ff, w_dt = _weights(w_gate, w_up, w_down, s_gate, s_up, s_down)
@@ -270,7 +279,7 @@ def moe_layer(logits, x, w_gate, w_up, w_down, k: int, out: dict, workspace: Wor
                   counts=(torch.int32, (E,)), offsets=(torch.int32, (E + 1,)),
                   sorted_to_flat=(torch.int32, (R,)), flat_to_sorted=(torch.int32, (R,)),
                   x_sorted=(x.dtype, (R, d)), y_sorted=(torch.float32, (R, d)),
-                  y=(torch.float32, (T, d)))
+                  y=(out["y"].dtype, (T, d)))
     for n, (dt, shp) in shapes.items():
         _need(out[n], dt, shp, n)
     o = out
@@ -279,14 +288,16 @@ def moe_layer(logits, x, w_gate, w_up, w_down, k: int, out: dict, workspace: Wor
     tail = (_ptr(w_gate), _ptr(w_up), _ptr(w_down), w_dt, _ptr(s_gate), _ptr(s_up), _ptr(s_down),
             _ptr(o["topk_ids"]), _ptr(o["topk_gates"]), _ptr(o["counts"]), _ptr(o["offsets"]),
             _ptr(o["sorted_to_flat"]), _ptr(o["flat_to_sorted"]), _ptr(o["x_sorted"]),
-            _ptr(o["y_sorted"]), _ptr(o["y"]), workspace.ptr, workspace.nbytes, _stream(stream))
+            _ptr(o["y_sorted"]), _ptr(o["y"]), _y_dt(o["y"]), workspace.ptr, workspace.nbytes,
+            _stream(stream))
     if capacity is None:
         _check(lib.moe_layer(*head, *tail))
     else:
         _check(lib.moe_layer_capped(*head, int(capacity), *tail))
 
 
-def layer_buffers(T: int, E: int, k: int, d: int, act_dtype, device="cuda") -> dict:
+def layer_buffers(T: int, E: int, k: int, d: int, act_dtype, device="cuda",
+                  y_dtype=torch.float32) -> dict:
     """Allocate (with torch) every output buffer moe_layer writes."""
     R = T * k
     z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
@@ -294,4 +305,4 @@ def layer_buffers(T: int, E: int, k: int, d: int, act_dtype, device="cuda") -> d
                 counts=z((E,), torch.int32), offsets=z((E + 1,), torch.int32),
                 sorted_to_flat=z((R,), torch.int32), flat_to_sorted=z((R,), torch.int32),
                 x_sorted=z((R, d), act_dtype), y_sorted=z((R, d), torch.float32),
-                y=z((T, d), torch.float32))
+                y=z((T, d), y_dtype))

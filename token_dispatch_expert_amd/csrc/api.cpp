@@ -118,9 +118,11 @@ moe_status_t check_ffn(const void* x_sorted, moe_dtype_t act, const int32_t* off
 }
 
 moe_status_t check_combine(const float* y_sorted, const int32_t* f2s, const float* gates, int T,
-                           int k, int d, const float* y) {
+                           int k, int d, const void* y, moe_dtype_t y_dtype) {
   if (T < 0 || k < 1 || k > MOE_MAX_TOPK || d < 1 || d > kMaxDim) return MOE_ERR_INVALID_ARG;
   if ((long long)T * k > INT_MAX) return MOE_ERR_INVALID_ARG;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16 && y_dtype != MOE_FP8_E4M3FN) return MOE_ERR_INVALID_ARG;
+  if (y_dtype == MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
   if (d % 4 != 0) return MOE_ERR_UNSUPPORTED;
   const long long R = (long long)T * k;
   if (!ok_ptr(y_sorted, R * d, 16) || !ok_ptr(f2s, R, 4) || !ok_ptr(gates, R, 4) ||
@@ -243,11 +245,12 @@ moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const 
 }
 
 moe_status_t moe_combine(const float* y_sorted, const int32_t* flat_to_sorted,
-                         const float* topk_gates, int T, int k, int d, float* y, void* stream) {
-  moe_status_t s = check_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y);
+                         const float* topk_gates, int T, int k, int d, void* y,
+                         moe_dtype_t y_dtype, void* stream) {
+  moe_status_t s = check_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y, y_dtype);
   if (s != MOE_OK) return s;
   return hip_status(moe::launch_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y,
-                                        static_cast<hipStream_t>(stream)));
+                                        y_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_layer_workspace_size(int T, int E, int k, int d, int d_ff, moe_dtype_t act_dtype,
@@ -263,8 +266,8 @@ moe_status_t moe_layer_capped(const float* logits, const void* x, moe_dtype_t ac
                        const float* s_up, const float* s_down, int32_t* topk_ids,
                        float* topk_gates, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
-                       float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       float* y_sorted, void* y, moe_dtype_t y_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
   moe_status_t s = check_route(logits, T, E, k, topk_ids, topk_gates, nullptr);
   if (s != MOE_OK) return s;
@@ -280,7 +283,7 @@ moe_status_t moe_layer_capped(const float* logits, const void* x, moe_dtype_t ac
   s = check_ffn(x_sorted, act_dtype, offsets, T * k, E, d, d_ff, w_gate, w_up, w_down, w_dtype,
                 s_gate, s_up, s_down, y_sorted, ws_ffn ? wsb + ws_perm : nullptr, ws_ffn);
   if (s != MOE_OK) return s;
-  s = check_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y);
+  s = check_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y, y_dtype);
   if (s != MOE_OK) return s;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -295,7 +298,8 @@ moe_status_t moe_layer_capped(const float* logits, const void* x, moe_dtype_t ac
   moe::FfnArgs a{x_sorted, act_dtype, offsets, T * k, E, d, d_ff, w_gate, w_up, w_down,
                  w_dtype, s_gate, s_up, s_down, y_sorted, wsb + ws_perm};
   if (moe::launch_grouped_ffn(a, dev, st) != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y, st));
+  return hip_status(moe::launch_combine(y_sorted, flat_to_sorted, topk_gates, T, k, d, y,
+                                        y_dtype == MOE_BF16, st));
 }
 
 moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype, int T, int E,
@@ -304,12 +308,12 @@ moe_status_t moe_layer(const float* logits, const void* x, moe_dtype_t act_dtype
                        const float* s_up, const float* s_down, int32_t* topk_ids,
                        float* topk_gates, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
-                       float* y_sorted, float* y, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       float* y_sorted, void* y, moe_dtype_t y_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   return moe_layer_capped(logits, x, act_dtype, T, E, k, d, d_ff, INT_MAX, w_gate, w_up, w_down,
                           w_dtype, s_gate, s_up, s_down, topk_ids, topk_gates, counts, offsets,
-                          sorted_to_flat, flat_to_sorted, x_sorted, y_sorted, y, workspace,
-                          workspace_bytes, stream);
+                          sorted_to_flat, flat_to_sorted, x_sorted, y_sorted, y, y_dtype,
+                          workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -11,6 +11,8 @@
 // gates are uniform per workgroup and come through scalar loads. Every y_sorted element is read
 // once and every y element written once, so both go through non-temporal accesses (streaming
 // cache policy): at the 8192-token prefill shape that took the kernel from 5.0 to 5.8 TB/s.
+// The output is the fp32 sum, or that sum rounded to bf16 (round to nearest even) when the
+// caller asks for bf16 output (half the write bytes).
 #include "moe_internal.h"
 
 namespace moe {
@@ -20,12 +22,12 @@ typedef float f32v4 __attribute__((ext_vector_type(4)));
 constexpr int kCombineThreads = 256;
 constexpr int kCombineBatch = 8;  // slots whose loads are in flight together
 
+template <bool BF16_OUT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float4* __restrict__ ys,
                                                                   const int32_t* __restrict__ f2s,
                                                                   const float* __restrict__ gates,
                                                                   int k, int vec_per_row, int R,
-                                                                  int slices,
-                                                                  float4* __restrict__ y) {
+                                                                  int slices, void* __restrict__ y) {
   const int t = blockIdx.x / slices;
   const int v = (blockIdx.x % slices) * kCombineThreads + threadIdx.x;
   if (v >= vec_per_row) return;
@@ -55,18 +57,27 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float4* 
       }
     }
   }
-  __builtin_nontemporal_store(f32v4{acc.x, acc.y, acc.z, acc.w},
-                              reinterpret_cast<f32v4*>(y + (size_t)t * vec_per_row + v));
+  if constexpr (BF16_OUT) {
+    // four bf16 values (RNE) in one 8-byte store
+    const __bf16 b[4] = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
+    unsigned long long bits;
+    __builtin_memcpy(&bits, b, 8);
+    __builtin_nontemporal_store(bits, reinterpret_cast<unsigned long long*>(y) + (size_t)t * vec_per_row + v);
+  } else {
+    __builtin_nontemporal_store(f32v4{acc.x, acc.y, acc.z, acc.w},
+                                reinterpret_cast<f32v4*>(y) + (size_t)t * vec_per_row + v);
+  }
 }
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* flat_to_sorted,
-                          const float* gates, int T, int k, int d, float* y, hipStream_t stream) {
+                          const float* gates, int T, int k, int d, void* y, bool bf16_out,
+                          hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int vpr = d / 4;
   const int slices = (vpr + kCombineThreads - 1) / kCombineThreads;
-  combine_kernel<<<(unsigned)T * slices, kCombineThreads, 0, stream>>>(
-      reinterpret_cast<const float4*>(y_sorted), flat_to_sorted, gates, k, vpr, T * k, slices,
-      reinterpret_cast<float4*>(y));
+  auto kern = bf16_out ? &combine_kernel<true> : &combine_kernel<false>;
+  kern<<<(unsigned)T * slices, kCombineThreads, 0, stream>>>(
+      reinterpret_cast<const float4*>(y_sorted), flat_to_sorted, gates, k, vpr, T * k, slices, y);
   return hipGetLastError();
 }
 

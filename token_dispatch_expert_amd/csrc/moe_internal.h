@@ -82,7 +82,8 @@ size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, mo
 hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* flat_to_sorted,
-                          const float* gates, int T, int k, int d, float* y, hipStream_t stream);
+                          const float* gates, int T, int k, int d, void* y, bool bf16_out,
+                          hipStream_t stream);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

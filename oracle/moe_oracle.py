@@ -209,8 +209,14 @@ def expert_ffn(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
         h = round_bf16_value(h)
     elif h_round is not None:
         raise ValueError(h_round)
-    y = h @ Wd.T
+    y = expert_down(h, Wd)
     return (y, h) if return_h else y
+
+
+def expert_down(h: np.ndarray, Wd: np.ndarray) -> np.ndarray:
+    """The down projection of one expert alone, y = h Wd (fp64; Wd stored [d, d_ff]): the
+    second GEMM of expert_ffn, also applied by the tests to another implementation's own h."""
+    return h @ Wd.T
 
 
 def ffn(x_sorted: np.ndarray, offsets: np.ndarray, expert_weights, return_h: bool = False,

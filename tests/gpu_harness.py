@@ -91,7 +91,13 @@ class DeviceWeights:
         return dict(self.scales) if self.scales is not None else {}
 
 
-def run_layer(cfg: synth.Config, logits: np.ndarray, x: np.ndarray, W: DeviceWeights, dev):
+def run_layer(cfg: synth.Config, logits: np.ndarray, x: np.ndarray, W: DeviceWeights, dev,
+              h_rows=None):
+    """moe_layer on the device; returns every output on the host. h_rows (optional, bf16
+    activations): sorted rows whose h (the bf16 SwiGLU activations between the two GEMMs) is
+    also returned, as bf16 bits under the key "h". h is read from the workspace, where the
+    header places it: the grouped FFN's workspace follows the permutation's, and h
+    [T*k, d_ff] opens it."""
     lg = torch.from_numpy(logits).to(dev)
     xd = to_dev(x, cfg.act, dev)
     out = layer_buffers(cfg.T, cfg.E, cfg.k, cfg.d, ACT_TORCH[cfg.act], device=dev)
@@ -105,7 +111,15 @@ def run_layer(cfg: synth.Config, logits: np.ndarray, x: np.ndarray, W: DeviceWei
     ws.buf.fill_(0xFF)
     moe.moe_layer(lg, xd, W.gate, W.up, W.down, cfg.k, out, ws, **W.kwargs())
     torch.cuda.synchronize()
-    return {n: to_host(t) for n, t in out.items()}
+    got = {n: to_host(t) for n, t in out.items()}
+    if h_rows is not None:
+        assert cfg.act == "bf16"
+        off = moe.moe_permute_workspace_size(cfg.T, cfg.E, cfg.k)
+        R = cfg.T * cfg.k
+        h = ws.buf[off:off + R * cfg.d_ff * 2].view(torch.int16).view(R, cfg.d_ff)
+        idx = torch.as_tensor(np.asarray(h_rows, np.int64), device=dev)
+        got["h"] = h.index_select(0, idx).cpu().numpy().view(np.uint16)
+    return got
 
 
 def check_routing_exact(got: dict, ref: dict, E: int):
@@ -148,10 +162,14 @@ def covering_tokens(cfg, perm, n_random, seed=0, block=128, small=16):
     return sorted(toks)
 
 
-def sampled_reference(toks, ids, gates, x, cfg, W, h_rounds=(None, "bf16")):
-    """The oracle's y rows and per-slot expert outputs for the listed tokens, for each h
-    rounding in h_rounds, decoding every expert's weights once (oracle.layer_tokens per
-    rounding would decode them twice). Returns {h_round: (y [len(toks), d], {(t, j): row})}."""
+def sampled_reference(toks, ids, gates, x, cfg, W, h_gpu=None):
+    """The oracle on the listed tokens only, decoding every expert's weights once. Returns a
+    dict with
+      y, rows        : y [len(toks), d] and {(t, j): y_sorted row} of the plain fp64 oracle;
+      y_bf16h, rows_bf16h : the same with h rounded to bf16 between the GEMMs (rounding point);
+      h64            : {(t, j): the slot's fp64 h row};
+    and, when h_gpu ({(t, j): the implementation's bf16 h row, as bits}) is given,
+      y_gpu_h, rows_gpu_h : the down projection and combine applied to those h rows."""
     k = cfg.k
     X = oracle.decode_activations(np.asarray(x)[toks], cfg.act)
     by_expert = {}
@@ -159,18 +177,52 @@ def sampled_reference(toks, ids, gates, x, cfg, W, h_rounds=(None, "bf16")):
         for j in range(k):
             by_expert.setdefault(int(ids[t, j]), []).append((ti, j))
     dec = oracle.make_weight_decoder(W.raw, cfg.w)
-    out = {}
-    ys = {hr: np.zeros((len(toks) * k, cfg.d)) for hr in h_rounds}
+    modes = ["plain", "bf16h"] + (["gpu_h"] if h_gpu is not None else [])
+    ys = {m: np.zeros((len(toks) * k, cfg.d)) for m in modes}
+    h64 = {}
     for e, items in sorted(by_expert.items()):
         Wg, Wu, Wd = dec(e)
         Xe = X[[ti for ti, _ in items]]
-        for hr in h_rounds:
-            Y = oracle.expert_ffn(Xe, Wg, Wu, Wd, h_round=hr)
-            for (ti, j), yr in zip(items, Y):
-                ys[hr][ti * k + j] = yr
+        Y, H64 = oracle.expert_ffn(Xe, Wg, Wu, Wd, return_h=True)
+        Yr = oracle.expert_ffn(Xe, Wg, Wu, Wd, h_round="bf16")
+        Yg = None
+        if h_gpu is not None:
+            Hg = oracle.decode_bf16(np.stack([h_gpu[(toks[ti], j)] for ti, j in items]))
+            Yg = oracle.expert_down(Hg, Wd)
+        for n, (ti, j) in enumerate(items):
+            ys["plain"][ti * k + j] = Y[n]
+            ys["bf16h"][ti * k + j] = Yr[n]
+            if Yg is not None:
+                ys["gpu_h"][ti * k + j] = Yg[n]
+            h64[(toks[ti], j)] = H64[n]
     f2s = np.arange(len(toks) * k, dtype=np.int32)
-    for hr in h_rounds:
-        y = oracle.combine(ys[hr], f2s, np.asarray(gates)[toks])
-        rows = {(t, j): ys[hr][ti * k + j] for ti, t in enumerate(toks) for j in range(k)}
-        out[hr] = (y, rows)
+    out = {"h64": h64}
+    for m, suffix in (("plain", ""), ("bf16h", "_bf16h"), ("gpu_h", "_gpu_h")):
+        if m not in ys:
+            continue
+        out["y" + suffix] = oracle.combine(ys[m], f2s, np.asarray(gates)[toks])
+        out["rows" + suffix] = {(t, j): ys[m][ti * k + j] for ti, t in enumerate(toks) for j in range(k)}
     return out
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values (8 significant bits) at the magnitude of each fp64 value."""
+    _, e = np.frexp(np.asarray(v, np.float64))  # v = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(1.0, e - 8)
+
+
+def check_h_rounding_point(h_gpu_bits: np.ndarray, h64: np.ndarray, name: str):
+    """The implementation's bf16 h against the fp64 h: every element within one bf16 unit of the
+    fp64 value (round to nearest of the fp32 result) plus an absolute allowance of 1e-4 rms(h)
+    for the fp32 accumulation of dot products that cancel to near zero, and at least 99% of the
+    elements exactly the nearest bf16 of the fp64 value."""
+    hg = oracle.decode_bf16(h_gpu_bits)
+    err = np.abs(hg - h64)
+    rms = float(np.sqrt(np.mean(h64 * h64)))
+    bound = bf16_ulp(h64) + 1e-4 * rms
+    worst = float(np.max(err / bound))
+    exact = float(np.mean(hg == oracle.round_bf16_value(h64)))
+    print(f"{name}: h vs fp64 h: worst |err| / (1 bf16 unit + 1e-4 rms) = {worst:.3f}; "
+          f"{exact:.5%} exactly the nearest bf16", flush=True)
+    assert worst <= 1.0, f"h element off by more than one bf16 unit ({worst:.3f} of the bound)"
+    assert exact >= 0.99, f"only {exact:.3%} of h elements are the nearest bf16 of the fp64 value"

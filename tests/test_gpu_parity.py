@@ -59,40 +59,53 @@ def run_full(cfg, dev, logits=None, x=None, plain_bar=True):
 
 def run_sampled(cfg, dev, n_tokens, seed=0):
     """Full-size layer: routing/permutation in full, float outputs on a token sample that
-    reaches every active expert, every row tile and every kernel role."""
+    reaches every active expert, every row tile and every kernel role.
+
+    Float bars on the sample: y and y_sorted within the workload's tolerance of the plain fp64
+    oracle; the implementation's bf16 h (its rounding point between the GEMMs) element by
+    element within one bf16 unit of the fp64 h; y_sorted within the fp32 bar (1e-5) of the
+    fp64 down projection of the implementation's own h, and y within it of their combine. (A
+    y-level comparison with a bf16-h oracle is statistical at this size: the rare h element
+    whose fp32 and fp64 values round to different bf16 neighbours moves its row's outputs by one
+    bf16 unit of h, and over thousands of rows the largest such move exceeds 5e-3 of rms.)"""
     logits, x = synth.make_routing_inputs(cfg)
     ref_ids, ref_gates = oracle.route(logits, cfg.k)
     perm = oracle.permute(ref_ids, cfg.E)
     W = H.DeviceWeights(cfg, dev, experts=H.active_experts(perm["counts"]))
+    toks = H.covering_tokens(cfg, perm, n_tokens, seed)
+    keys = [(t, j) for t in toks for j in range(cfg.k)]
+    srows = [int(perm["flat_to_sorted"][t * cfg.k + j]) for t, j in keys]
     print(f"{cfg.name}: weights on the device, running the layer", flush=True)
-    got = H.run_layer(cfg, logits, x, W, dev)
+    got = H.run_layer(cfg, logits, x, W, dev, h_rows=srows if cfg.act == "bf16" else None)
     H.check_routing_exact(got, dict(topk_ids=ref_ids, **perm), cfg.E)
     H.check_gates(got["topk_gates"], ref_gates, cfg.k)
     xs_ref = oracle.gather_rows(x, perm["sorted_to_flat"], cfg.k)
     assert np.array_equal(got["x_sorted"], xs_ref), "x_sorted bytes differ"
     assert np.all(np.isfinite(got["y"])), "non-finite output (an expert without rows was read?)"
-    toks = H.covering_tokens(cfg, perm, n_tokens, seed)
     print(f"{cfg.name}: routing exact; oracle on {len(toks)} tokens", flush=True)
-    refs = H.sampled_reference(toks, ref_ids, ref_gates, x, cfg, W)
-    y_ref, rows = refs[None]
-    keys = sorted(rows)
-    ys_got = np.stack([got["y_sorted"][perm["flat_to_sorted"][t * cfg.k + j]] for t, j in keys])
+    h_gpu = {key: got["h"][n] for n, key in enumerate(keys)} if "h" in got else None
+    ref = H.sampled_reference(toks, ref_ids, ref_gates, x, cfg, W, h_gpu=h_gpu)
+    ys_got = got["y_sorted"][srows]
     tol = H.TOL[cfg.w]
-    e_y = oracle.rel_max_err(got["y"][toks], y_ref)
-    e_ys = oracle.rel_max_err(ys_got, np.stack([rows[key] for key in keys]))
-    covered = {int(np.searchsorted(perm["offsets"], perm["flat_to_sorted"][t * cfg.k + j], side="right")) - 1
-               for t, j in keys}
+    e_y = oracle.rel_max_err(got["y"][toks], ref["y"])
+    e_ys = oracle.rel_max_err(ys_got, np.stack([ref["rows"][key] for key in keys]))
+    covered = {int(np.searchsorted(perm["offsets"], r, side="right")) - 1 for r in srows}
     active = set(H.active_experts(perm["counts"]))
     print(f"{cfg.name}: {len(toks)} sampled tokens, {len(keys)} y_sorted rows of {len(covered)}/{len(active)} "
           f"active experts: y_sorted err {e_ys:.3e}, y err {e_y:.3e} (tol {tol})", flush=True)
+    e_ys2 = oracle.rel_max_err(ys_got, np.stack([ref["rows_bf16h"][key] for key in keys]))
+    e_y2 = oracle.rel_max_err(got["y"][toks], ref["y_bf16h"])
+    print(f"{cfg.name}: vs bf16-h oracle (figure only): y_sorted err {e_ys2:.3e}, y err {e_y2:.3e}", flush=True)
     assert covered == active, "the sample misses an active expert"
     assert e_ys <= tol and e_y <= tol
-    y_ref2, rows2 = refs["bf16"]
-    e_y2 = oracle.rel_max_err(got["y"][toks], y_ref2)
-    e_ys2 = oracle.rel_max_err(ys_got, np.stack([rows2[key] for key in keys]))
-    print(f"{cfg.name}: vs bf16-h oracle: y_sorted err {e_ys2:.3e}, y err {e_y2:.3e} "
-          f"(tol {H.TOL_ROUNDING_POINT})", flush=True)
-    assert e_ys2 <= H.TOL_ROUNDING_POINT and e_y2 <= H.TOL_ROUNDING_POINT
+    if h_gpu is not None:
+        H.check_h_rounding_point(np.stack([h_gpu[key] for key in keys]),
+                                 np.stack([ref["h64"][key] for key in keys]), cfg.name)
+        e_ys3 = oracle.rel_max_err(ys_got, np.stack([ref["rows_gpu_h"][key] for key in keys]))
+        e_y3 = oracle.rel_max_err(got["y"][toks], ref["y_gpu_h"])
+        print(f"{cfg.name}: vs fp64 down projection + combine of the GPU's own h: y_sorted err {e_ys3:.3e}, "
+              f"y err {e_y3:.3e} (tol {H.TOL['f32']})", flush=True)
+        assert e_ys3 <= H.TOL["f32"] and e_y3 <= H.TOL["f32"]
 
 
 # ----------------------------------------------------------------------------------------

@@ -401,7 +401,7 @@ def test_oracle_pin(check):
 # the pins must catch plausible mistakes planted in the oracle
 # ----------------------------------------------------------------------------------------
 _ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16",
-                                     "expert_capacity", "router_logits", "rel_max_err")}
+                                     "expert_capacity", "router_logits", "rel_max_err", "expert_down")}
 
 
 def _mut_route_tie_high(logits, k):
@@ -542,6 +542,15 @@ def _mut_router_untransposed_rows(x, x_fmt, w_router, w_fmt):
     return X @ Wr[::-1].T
 
 
+def _mut_down_reversed_inputs(h, Wd):
+    # h's columns paired with the wrong rows of the stored down matrix
+    return h[:, ::-1] @ Wd.T
+
+
+def _mut_down_missing_last(h, Wd):
+    return h[:, :-1] @ Wd[:, :-1].T
+
+
 def _mut_err_mean(got, ref):
     # mean |error| in place of the largest
     ref, got = np.asarray(ref, np.float64), np.asarray(got, np.float64)
@@ -584,6 +593,8 @@ MUTANTS = {
     "combine_wrong_map": ("combine", _mut_combine_wrong_map),
     "decode_bf16_shift": ("decode_bf16", _mut_decode_bf16_shift),
     "decode_e4m3_bias8": ("decode_e4m3fn", _mut_decode_e4m3_bias8),
+    "down_reversed_inputs": ("expert_down", _mut_down_reversed_inputs),
+    "down_missing_last": ("expert_down", _mut_down_missing_last),
     "rel_err_mean": ("rel_max_err", _mut_err_mean),
     "rel_err_max_ref": ("rel_max_err", _mut_err_max_ref),
     "rel_err_no_sqrt": ("rel_max_err", _mut_err_no_sqrt),

@@ -99,10 +99,40 @@ def test_sampled_reference_matches_layer():
         a, b = int(perm["offsets"][e]), int(perm["offsets"][e + 1])
         want = set(range(a, b)) if b - a <= 4 else set(range(a, b, 8)) | ({b - 1} if b > a else set())
         assert want <= owned
-    refs = H.sampled_reference(toks, ids, gates, x, cfg, W)
-    for hr in (None, "bf16"):
+    # h from a bf16 implementation that rounds the fp64 h: its down projection is the bf16-h oracle
+    full_h = oracle.layer(logits, x, "bf16", W.raw, "bf16", cfg.k, return_h=True)
+    h_bits = {(t, j): synth.round_to_bf16(full_h["h"][full_h["flat_to_sorted"][t * cfg.k + j]].astype(np.float32))
+              for t in toks for j in range(cfg.k)}
+    ref = H.sampled_reference(toks, ids, gates, x, cfg, W, h_gpu=h_bits)
+    for hr, suffix in ((None, ""), ("bf16", "_bf16h")):
         full = oracle.layer(logits, x, "bf16", W.raw, "bf16", cfg.k, h_round=hr)
-        y, rows = refs[hr]
-        assert np.allclose(y, full["y"][toks], rtol=1e-12, atol=1e-12)
-        for (t, j), yr in rows.items():
+        assert np.allclose(ref["y" + suffix], full["y"][toks], rtol=1e-12, atol=1e-12)
+        for (t, j), yr in ref["rows" + suffix].items():
             assert np.allclose(yr, full["y_sorted"][full["flat_to_sorted"][t * cfg.k + j]], rtol=1e-12, atol=1e-12)
+    for (t, j), h in ref["h64"].items():
+        assert np.allclose(h, full_h["h"][full_h["flat_to_sorted"][t * cfg.k + j]], rtol=1e-12, atol=1e-14)
+    # fp32 rounding of the fp64 h then RNE to bf16 is at most one double rounding away from the
+    # bf16-h oracle's rounding: the rows agree within a bf16 unit's effect
+    near = oracle.rel_max_err(ref["y_gpu_h"], ref["y_bf16h"])
+    assert near <= 1e-2
+    H.check_h_rounding_point(np.stack([h_bits[key] for key in sorted(h_bits)]),
+                             np.stack([ref["h64"][key] for key in sorted(h_bits)]), "tiny")
+
+
+def test_h_rounding_point_check_catches_mistakes():
+    # the GPU tests' element-wise check of the implementation's bf16 h fails for an element two
+    # bf16 units off, and for truncation in place of round-to-nearest
+    import pytest
+    import gpu_harness as H
+    rng = np.random.default_rng(3)
+    h64 = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-3, 3, (64, 1)))
+    good = synth.round_to_bf16(h64.astype(np.float32))
+    H.check_h_rounding_point(good, h64, "good")
+    bad = good.copy()
+    i = np.unravel_index(np.argmax(np.abs(h64)), h64.shape)  # an element far above the allowance
+    bad[i] = np.uint16(bad[i] + 2)
+    with pytest.raises(AssertionError):
+        H.check_h_rounding_point(bad, h64, "two units off")
+    trunc = (h64.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    with pytest.raises(AssertionError):
+        H.check_h_rounding_point(trunc, h64, "truncated")

@@ -128,6 +128,26 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, const int32_t* topk
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc - moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): no workspace
+ * argument, and no allocation of any kind. Its scratch (the per-tile histograms and bases,
+ * moe_permute_workspace_size(T, E, k) bytes) is a static device array of
+ * MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4 MiB) that each GPU holds from the first call on that
+ * GPU until the process ends; sizes whose workspace would exceed it return MOE_ERR_WORKSPACE
+ * before anything is enqueued (with E = 256 that is T*k above 1,048,576 assignments). The array keeps the last
+ * call's contents and needs no clearing (every entry read is written first within the call).
+ * All calls on one GPU share the array: calls that overlap on one GPU (on different streams,
+ * without ordering between them) race and give undefined results. Arguments, outputs and
+ * other errors as moe_permute; the first call on a GPU also looks up the array's device
+ * address (MOE_ERR_HIP if that fails).
+ */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status_t moe_permute_noalloc(const void* x, moe_dtype_t x_dtype, const int32_t* topk_ids,
+                                 int T, int E, int k, int d, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                                 void* stream);
+
+/*
  * moe_expert_capacity - ceil(C * T * k / E), the per-expert capacity for a capacity factor
  * C = factor_percent / 100 (tutorial page, section 5, mitigation 1: capacity = C x tokens / E,
  * here counting the T*k assignments; section 10, exercise D sweeps C from 1.0 to 2.0). Exact

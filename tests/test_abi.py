@@ -211,3 +211,15 @@ def test_route_gemm_rejects_bad_arguments(lib):
     assert call(logits=MIS) == B.MOE_ERR_INVALID_ARG
     assert call(ws=None) == B.MOE_ERR_WORKSPACE
     assert call(wsb=wsb - 4) == B.MOE_ERR_WORKSPACE
+
+
+def test_noalloc_permute_rejects_bad_arguments(lib):
+    f = lib.moe_permute_noalloc
+    # the per-tile counts of 4,097 tiles x 256 experts exceed the 4 MiB static scratch
+    T, E, k, d = (1 << 20) // 8 + 32, 256, 8, 8
+    assert lib.moe_permute_workspace_size(T, E, k) > B.PERMUTE_NOALLOC_SCRATCH_BYTES
+    assert f(P, B.MOE_BF16, P2, T, E, k, d, P3, P3, P3, P3, P, None) == B.MOE_ERR_WORKSPACE
+    assert f(None, B.MOE_BF16, P2, 64, 8, 2, 128, P3, P3, P3, P3, P, None) == B.MOE_ERR_INVALID_ARG
+    assert f(P, B.MOE_FP8_E4M3FN, P2, 64, 8, 2, 128, P3, P3, P3, P3, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(P, B.MOE_BF16, P2, 64, 8, 9, 128, P3, P3, P3, P3, P, None) == B.MOE_ERR_INVALID_ARG
+

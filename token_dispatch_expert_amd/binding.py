@@ -27,7 +27,7 @@ ENTRY_POINTS = (
     "moe_status_string", "moe_route", "moe_permute_workspace_size", "moe_permute",
     "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
     "moe_layer", "moe_expert_capacity", "moe_permute_capped", "moe_layer_capped",
-    "moe_route_gemm", "moe_route_gemm_workspace_size",
+    "moe_route_gemm", "moe_route_gemm_workspace_size", "moe_permute_noalloc",
 )
 
 _lib = None
@@ -68,6 +68,7 @@ def load_library(path: str | None = None):
         "moe_route_gemm": ([P, I, P, I, I, I, I, I, P, P, P, P, P, S, P], I),
         "moe_route_gemm_workspace_size": ([I, I, I], S),
         "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
+        "moe_permute_noalloc": ([P, I, P, I, I, I, I, P, P, P, P, P, P], I),
         "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
                               P, P, P, P, P, P, P, P, P, I, P, S, P], I),
     }
@@ -206,6 +207,27 @@ def moe_permute(x, topk_ids, E: int, counts, offsets, sorted_to_flat, flat_to_so
         _check(lib.moe_permute(*head, *tail))
     else:
         _check(lib.moe_permute_capped(*head, int(capacity), *tail))
+
+
+def moe_permute_noalloc(x, topk_ids, E: int, counts, offsets, sorted_to_flat, flat_to_sorted,
+                        x_sorted, stream=None):
+    """moe_permute without a workspace: the library's static per-GPU scratch (no allocation)."""
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    R = T * k
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(counts, torch.int32, (E,), "counts")
+    _need(offsets, torch.int32, (E + 1,), "offsets")
+    _need(sorted_to_flat, torch.int32, (R,), "sorted_to_flat")
+    _need(flat_to_sorted, torch.int32, (R,), "flat_to_sorted")
+    _need(x_sorted, x.dtype, (R, d), "x_sorted")
+    _check(load_library().moe_permute_noalloc(
+        _ptr(x), _dt(x, "x"), _ptr(topk_ids), T, E, k, d, _ptr(counts), _ptr(offsets),
+        _ptr(sorted_to_flat), _ptr(flat_to_sorted), _ptr(x_sorted), _stream(stream)))
+
+
+# bytes of the static scratch behind moe_permute_noalloc (MOE_PERMUTE_NOALLOC_SCRATCH_BYTES)
+PERMUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 def moe_expert_capacity(T: int, E: int, k: int, factor_percent: int) -> int:

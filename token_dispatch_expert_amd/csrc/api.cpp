@@ -66,10 +66,9 @@ moe_status_t check_route(const float* logits, int T, int E, int k, const int32_t
   return MOE_OK;
 }
 
-moe_status_t check_permute(const void* x, moe_dtype_t x_dt, const int32_t* ids, int T, int E,
-                           int k, int d, const int32_t* counts, const int32_t* offsets,
-                           const int32_t* s2f, const int32_t* f2s, const void* x_sorted,
-                           const void* ws, size_t ws_bytes) {
+moe_status_t check_permute_io(const void* x, moe_dtype_t x_dt, const int32_t* ids, int T, int E,
+                              int k, int d, const int32_t* counts, const int32_t* offsets,
+                              const int32_t* s2f, const int32_t* f2s, const void* x_sorted) {
   moe_status_t s = check_sizes(T, E, k);
   if (s != MOE_OK) return s;
   if (d < 1 || d > kMaxDim) return MOE_ERR_INVALID_ARG;
@@ -80,6 +79,15 @@ moe_status_t check_permute(const void* x, moe_dtype_t x_dt, const int32_t* ids, 
       !ok_ptr(offsets, E + 1, 4) || !ok_ptr(s2f, R, 4) || !ok_ptr(f2s, R, 4) ||
       !ok_ptr(x_sorted, R * d, 16))
     return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t check_permute(const void* x, moe_dtype_t x_dt, const int32_t* ids, int T, int E,
+                           int k, int d, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* s2f, const int32_t* f2s, const void* x_sorted,
+                           const void* ws, size_t ws_bytes) {
+  moe_status_t s = check_permute_io(x, x_dt, ids, T, E, k, d, counts, offsets, s2f, f2s, x_sorted);
+  if (s != MOE_OK) return s;
   const size_t need = moe_permute_workspace_size(T, E, k);
   if (need > 0 && (ws == nullptr || !aligned(ws, 16) || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
@@ -194,6 +202,25 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, const int32_t* topk
   return moe_permute_capped(x, x_dtype, topk_ids, T, E, k, d, INT_MAX, counts, offsets,
                             sorted_to_flat, flat_to_sorted, x_sorted, workspace, workspace_bytes,
                             stream);
+}
+
+static_assert(moe::kStaticPermuteInts * sizeof(int32_t) == MOE_PERMUTE_NOALLOC_SCRATCH_BYTES,
+              "the static scratch is the size the header states");
+
+moe_status_t moe_permute_noalloc(const void* x, moe_dtype_t x_dtype, const int32_t* topk_ids,
+                                 int T, int E, int k, int d, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
+                                 void* stream) {
+  moe_status_t s = check_permute_io(x, x_dtype, topk_ids, T, E, k, d, counts, offsets,
+                                    sorted_to_flat, flat_to_sorted, x_sorted);
+  if (s != MOE_OK) return s;
+  // the per-tile counts must fit the static scratch (checked before any HIP call)
+  if (moe_permute_workspace_size(T, E, k) > MOE_PERMUTE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int32_t* scratch = nullptr;
+  if (moe::permute_static_scratch(&scratch) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_permute(x, act_bytes(x_dtype), topk_ids, T, E, k, d, INT_MAX,
+                                        counts, offsets, sorted_to_flat, flat_to_sorted, x_sorted,
+                                        scratch, static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_capacity(int T, int E, int k, int factor_percent) {

@@ -63,6 +63,11 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
                           int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted,
                           int32_t* ws, hipStream_t stream);
 
+// No-allocation permutation: the device address of this GPU's static scratch array of
+// kStaticPermuteInts int32 (looked up once per device, with that device current, and cached).
+constexpr size_t kStaticPermuteInts = size_t(1) << 20;  // 4 MiB
+hipError_t permute_static_scratch(int32_t** out);
+
 struct FfnArgs {
   const void* x_sorted;
   moe_dtype_t act;

@@ -26,6 +26,8 @@
 //          the group's last lane advances the running base in LDS. Writes both index maps.
 //   copy : one workgroup per token reads x[t] once in 16-byte vectors and stores it to its
 //          k sorted rows.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -347,6 +349,33 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void permute_small_kernel(
       f2s[i] = keep ? pos : -1;
     }
   }
+}
+
+// Scratch of the no-allocation entry point: the per-tile histograms and bases (the same
+// n_tiles * E int32 as the caller's workspace of moe_permute) in a file-scope device array,
+// kStaticPermuteInts entries. Every GPU the library runs on holds its own copy until the
+// process ends. The histogram launch writes every entry the later launches read, so nothing
+// needs clearing between calls; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) int32_t scratch[kStaticPermuteInts];
+
+hipError_t permute_static_scratch(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* ptrs[64] = {};
+  int dev = 0;
+  hipError_t st = hipGetDevice(&dev);
+  if (st != hipSuccess) return st;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    // the device address of this GPU's copy (the array's name in host code is only a handle)
+    void* p = nullptr;
+    st = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (st != hipSuccess) return st;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int T, int E, int k,

@@ -95,26 +95,77 @@ def _time_calls(fn, reps: int, warmup: int = 2) -> list:
     return out
 
 
+def fit_max_affine(P):
+    """One max-affine model t = max(a + b*G, c + beta*N) over every point (G active experts, N
+    rows in all, time t): the two branches are first fitted by least squares on the points each
+    one wins, alternating until the assignment settles; the four parameters are then refined to
+    minimise the largest relative misfit (Nelder-Mead). Returns (a, b, c, beta, max_rel_misfit,
+    rms_rel_misfit)."""
+    import numpy as np
+    from scipy.optimize import minimize
+    G, N, t = P[:, 0], P[:, 1], P[:, 2]
+    small = P[:, 1] / P[:, 0] <= 8
+    for _ in range(20):
+        A1 = np.stack([np.ones(small.sum()), G[small]], 1)
+        A2 = np.stack([np.ones((~small).sum()), N[~small]], 1)
+        w1, w2 = 1.0 / t[small], 1.0 / t[~small]     # relative least squares
+        a, b = np.linalg.lstsq(A1 * w1[:, None], t[small] * w1, rcond=None)[0]
+        c, beta = np.linalg.lstsq(A2 * w2[:, None], t[~small] * w2, rcond=None)[0]
+        new_small = (a + b * G) >= (c + beta * N)
+        if np.array_equal(new_small, small) or new_small.all() or (~new_small).all():
+            break
+        small = new_small
+
+    def misfit(th):
+        m = np.maximum(th[0] + th[1] * G, th[2] + th[3] * N)
+        return np.max(np.abs(m - t) / t)
+
+    th = minimize(misfit, np.array([a, b, c, beta]), method="Nelder-Mead",
+                  options={"maxiter": 20000, "xatol": 1e-9, "fatol": 1e-9}).x
+    m = np.maximum(th[0] + th[1] * G, th[2] + th[3] * N)
+    rel = (m - t) / t
+    return (*[float(v) for v in th], float(np.max(np.abs(rel))), float(np.sqrt(np.mean(rel * rel))))
+
+
 def expert_time_sweep(args) -> int:
     """Expert-time profile of moe_grouped_ffn (the makespan abstract's max-affine model on this
-    GPU): G active experts with n rows each, every other expert empty, at the decode (d=4096,
-    d_ff=1536, E=128) and DeepSeek-V3 (d=7168, d_ff=2048, E=256) shapes, bf16. Fits
-    t = max(a + b*G, c + beta*N) (N = G*n rows) and reports n* = b / beta, the row count where
-    an expert's time stops being its weight streaming."""
+    GPU): G active experts with n rows each (n up to 4096), every other expert empty, at the
+    decode (d=4096, d_ff=1536, E=128, bf16) and DeepSeek-V3 (d=7168, d_ff=2048, E=256) shapes,
+    the latter with bf16 and with fp8 e4m3fn weights (128 x 128 block scales). One max-affine
+    model t = max(a + b*G, c + beta*N) (N = G*n rows) is fitted over all points of a shape;
+    n* = b / beta is the row count where an expert's time stops being its weight streaming
+    (compared with the HBM/MFMA ridge of the weight format: ~312 rows bf16, ~156 fp8).
+    Then the tutorial's exercise A on the routing side: active experts and load imbalance
+    (max / mean assignments per expert) against batch size T in {1, 16, 128, 1024} under the
+    decode and prefill workloads' Zipf logit biases, routed by moe_route on the GPU."""
     import numpy as np
     import torch
+    import synth
     import token_dispatch_expert_amd as moe
     dev = torch.device("cuda:0")
-    ns = [1, 2, 4, 8, 16, 32, 64, 128, 192, 256, 384, 512, 768, 1024, 2048]
+    ns = [1, 2, 4, 8, 16, 32, 64, 96, 128, 160, 192, 256, 320, 384, 512, 768, 1024, 2048, 4096]
     Gs = [1, 4, 16, 64]
-    shapes = [("decode Qwen3-like", 4096, 1536, 128), ("DeepSeek-V3-like", 7168, 2048, 256)]
+    shapes = [("decode Qwen3-like, bf16 weights", 4096, 1536, 128, "bf16"),
+              ("DeepSeek-V3-like, bf16 weights", 7168, 2048, 256, "bf16"),
+              ("DeepSeek-V3-like, fp8 e4m3fn weights", 7168, 2048, 256, "fp8")]
     result = {"metric": "grouped-FFN time vs rows per expert and active experts",
-              "unit": "us", "dtype": "bf16", "data": "synthetic N(0,1) x, N(0,1/fan_in) weights",
+              "unit": "us", "data": "synthetic N(0,1) x, N(0,1/fan_in) weights (fp8: scaled codes)",
+              "timing": "median of per-call GPU times (HIP events, each call enqueued behind a spin kernel)",
               "shapes": []}
-    for name, d, d_ff, E in shapes:
+    for name, d, d_ff, E, wfmt in shapes:
         g = torch.Generator(device=dev).manual_seed(0)
-        W = [torch.randn((E, a, b), generator=g, device=dev, dtype=torch.float32).div_(b ** 0.5).to(torch.bfloat16)
-             for a, b in ((d_ff, d), (d_ff, d), (d, d_ff))]
+        skw = {}
+        if wfmt == "bf16":
+            W = [torch.randn((E, a, b), generator=g, device=dev, dtype=torch.float32).div_(b ** 0.5).to(torch.bfloat16)
+                 for a, b in ((d_ff, d), (d_ff, d), (d, d_ff))]
+            ridge = 2500e12 / 8e12
+        else:
+            W = [torch.randn((E, a, b), generator=g, device=dev, dtype=torch.float32).mul_(64.0)
+                 .clamp_(-448, 448).to(torch.float8_e4m3fn) for a, b in ((d_ff, d), (d_ff, d), (d, d_ff))]
+            skw = {"s_gate": torch.full((E, d_ff // 128, d // 128), 1.0 / (64 * d ** 0.5), device=dev),
+                   "s_up": torch.full((E, d_ff // 128, d // 128), 1.0 / (64 * d ** 0.5), device=dev),
+                   "s_down": torch.full((E, d // 128, d_ff // 128), 1.0 / (64 * d_ff ** 0.5), device=dev)}
+            ridge = 2500e12 / 8e12 / 2
         pts = []
         for G in Gs:
             for n in ns:
@@ -126,34 +177,51 @@ def expert_time_sweep(args) -> int:
                 offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
                 xs = torch.randn((rows, d), generator=g, device=dev).to(torch.bfloat16)
                 ys = torch.empty((rows, d), device=dev)
-                ws = moe.Workspace(moe.moe_ffn_workspace_size(rows, E, d, d_ff, torch.bfloat16, torch.bfloat16), device=dev)
-                t = _time_calls(lambda: moe.moe_grouped_ffn(xs, offs, W[0], W[1], W[2], ys, ws), max(args.steps // 2, 5))
+                ws = moe.Workspace(moe.moe_ffn_workspace_size(rows, E, d, d_ff, torch.bfloat16, W[0].dtype), device=dev)
+                t = _time_calls(lambda: moe.moe_grouped_ffn(xs, offs, W[0], W[1], W[2], ys, ws, **skw),
+                                max(args.steps // 2, 5))
                 us = float(np.median(t))
                 pts.append((G, n, rows, us))
                 log(f"{name}: G={G} n={n}: {us:.1f} us")
                 del xs, ys, ws
-        # fit: the streaming branch on the small-n points, the row branch on the large-n points
-        P = np.array(pts, dtype=np.float64)
-        small = P[P[:, 1] <= 8]
-        large = P[P[:, 1] >= 1024]
-        A1 = np.stack([np.ones(len(small)), small[:, 0]], 1)
-        a, b = np.linalg.lstsq(A1, small[:, 3], rcond=None)[0]
-        A2 = np.stack([np.ones(len(large)), large[:, 2]], 1)
-        c, beta = np.linalg.lstsq(A2, large[:, 3], rcond=None)[0]
-        model = np.maximum(a + b * P[:, 0], c + beta * P[:, 2])
-        wbytes = 3 * d * d_ff * 2
+        P = np.array([(G, N, us) for G, _, N, us in pts], dtype=np.float64)
+        a, b, c, beta, mx, rms = fit_max_affine(P)
+        wbytes = 3 * d * d_ff * (2 if wfmt == "bf16" else 1)
         result["shapes"].append({
-            "shape": name, "d": d, "d_ff": d_ff, "E": E,
+            "shape": name, "d": d, "d_ff": d_ff, "E": E, "weights": wfmt,
             "points": [{"G": int(G), "n": int(n), "us": round(us, 2)} for G, n, _, us in pts],
             "fit": {"a_us": round(a, 2), "b_us_per_expert": round(b, 3), "c_us": round(c, 2),
-                    "beta_us_per_row": round(beta, 5),
-                    "max_rel_misfit": round(float(np.max(np.abs(model - P[:, 3]) / P[:, 3])), 3)},
+                    "beta_us_per_row": round(beta, 5), "max_rel_misfit": round(mx, 3),
+                    "rms_rel_misfit": round(rms, 3)},
             "n_star_measured": round(b / beta, 1),
+            "crossover_rows_per_expert_at_G": {str(G): round((a - c) / (beta * G) + b / beta, 1) for G in Gs},
             "per_expert_stream_GBps": round(wbytes / (b * 1e-6) / 1e9, 1),
             "row_rate_TFLOPs": round(6 * d * d_ff / (beta * 1e-6) / 1e12, 1),
-            "n_star_roofline_bf16": round(2500e12 / 8e12, 1)})
-        del W
+            "n_star_roofline": round(ridge, 1)})
+        log(f"{name}: fit max|misfit| {mx:.1%}, n* = {b / beta:.0f} rows (ridge {ridge:.0f})")
+        del W, skw
         torch.cuda.empty_cache()
+    # exercise A: imbalance vs batch size under the workloads' logit biases
+    ex = []
+    for wl in ("c2", "c3", "c4"):
+        base = synth.CONFIGS[wl]
+        for T in (1, 16, 128, 1024):
+            cfg = base.with_(T=T, name=f"{wl}-T{T}")
+            logits, _ = synth.make_routing_inputs(cfg)
+            lg = torch.from_numpy(logits).to(dev)
+            ids = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+            gates = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+            counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+            moe.moe_route(lg, cfg.k, ids, gates, counts)
+            c = counts.cpu().numpy().astype(np.int64)
+            mean = T * cfg.k / cfg.E
+            act = c[c > 0]
+            ex.append({"bias": f"{wl} (E={cfg.E}, k={cfg.k}, Zipf s={cfg.zipf_s})", "T": T,
+                       "active_experts": int(len(act)), "max_rows": int(c.max()),
+                       "max_over_mean": round(float(c.max() / mean), 2),
+                       "max_over_mean_active": round(float(c.max() / act.mean()), 2)})
+            log(f"exercise A {wl} T={T}: {len(act)} active, max/mean {c.max() / mean:.2f}")
+    result["exercise_A"] = ex
     print(json.dumps(result), flush=True)
     return 0
 

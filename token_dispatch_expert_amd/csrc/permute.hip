@@ -12,20 +12,23 @@
 // Every position is still ranked among all of the expert's assignments, and a position at or
 // past the expert's capped end is dropped, so capping costs nothing extra.
 //
-// Batches of more than kSmallR assignments take four launches, none using float atomics, all
-// deterministic (smaller batches use one workgroup for the first three, see
+// Batches of more than kSmallR assignments take three launches, none using float atomics, all
+// deterministic (smaller batches use one workgroup for the index work, see
 // permute_small_kernel):
 //   hist : one workgroup per tile of kPermuteTile flat entries; LDS histogram -> ws[tile][e]
-//   scan : one workgroup per kScanExperts experts; per expert an exclusive prefix over the
-//          tiles (groups of threads take ranges of tiles) -> ws[tile][e], relative to the
-//          expert's first row, and the kept count -> counts[e]
-//   rank : one wavefront per tile; it first scans the kept counts over the experts (offsets;
-//          the first tile's wavefront also stores them), then walks its entries in flat order,
-//          64 at a time; lanes with the same expert find each other with ballots over the
-//          expert id's bits, so a lane's rank among equal keys is a popcount of lower lanes;
-//          the group's last lane advances the running base in LDS. Writes both index maps.
+//   rank : one 1024-thread workgroup per tile. It sums, per expert, the histograms of the tiles
+//          before its own (its base inside the expert) and of all tiles (the expert's count,
+//          capped), threads splitting the tiles into slices and adding the slices in LDS; a
+//          block scan of the kept counts gives the expert offsets (the first tile's workgroup
+//          stores counts and offsets). Its first wavefront then walks the tile's entries in
+//          flat order, 64 at a time; lanes with the same expert find each other with ballots
+//          over the expert id's bits, so a lane's rank among equal keys is a popcount of lower
+//          lanes; the group's last lane advances the running position in LDS. Writes both
+//          index maps.
 //   copy : one workgroup per token reads x[t] once in 16-byte vectors and stores it to its
 //          k sorted rows.
+// (A separate scan launch between hist and rank, with the expert offsets scanned again by
+// every rank wavefront, took one more dependent launch: ~6 us of the 8192-token index phase.)
 #include <mutex>
 
 #include "moe_internal.h"
@@ -89,157 +92,106 @@ __device__ __forceinline__ int block_inclusive_scan_1024(int v, int32_t* wave_su
   return v + (wave > 0 ? wave_sum[wave - 1] : 0);
 }
 
-// Workgroup b takes experts b*kScanExperts .. +kScanExperts-1; its threads are kScanGroups
-// groups of kScanExperts, and group g takes a contiguous range of tiles, so thread (g, e) scans
-// at most kScanRegTiles tile counts of expert e in registers (all loaded at once). Group totals
-// give each group's base; the expert's total, capped, is its kept count. The scan over the
-// experts (offsets) is left to the rank kernel, so no single workgroup reads every tile.
-constexpr int kScanExperts = 16;
-constexpr int kScanGroups = 16;
-constexpr int kScanWgThreads = kScanExperts * kScanGroups;
-__global__ __launch_bounds__(kScanWgThreads) void permute_scan_kernel(int32_t* __restrict__ ws,
-                                                                      int n_tiles, int E, int cap,
-                                                                      int32_t* __restrict__ counts,
-                                                                      int32_t* __restrict__ offsets) {
-  __shared__ int32_t gsum[kScanWgThreads];  // [group][expert] group totals
-  const int tid = threadIdx.x;
-  const int g = tid / kScanExperts, el = tid - g * kScanExperts;
-  const int e = blockIdx.x * kScanExperts + el;
-  const bool active = e < E;
-  const int tpg = (n_tiles + kScanGroups - 1) / kScanGroups;
-  const int t0 = min(g * tpg, n_tiles), t1 = min(t0 + tpg, n_tiles);
-  const bool in_regs = tpg <= kScanRegTiles;
-  int pre[kScanRegTiles];
-  int run = 0;  // exclusive prefix within the group, then the group total
-  if (active) {
-    if (in_regs) {
-#pragma unroll
-      for (int u = 0; u < kScanRegTiles; ++u) pre[u] = t0 + u < t1 ? ws[(size_t)(t0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < kScanRegTiles; ++u) {
-        const int h = pre[u];
-        pre[u] = run;
-        run += h;
-      }
-    } else {
-      constexpr int B = 16;  // batches of independent loads
-      for (int tb = t0; tb < t1; tb += B) {
-        int h[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) h[u] = (tb + u < t1) ? ws[(size_t)(tb + u) * E + e] : 0;
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-          if (tb + u < t1) {
-            ws[(size_t)(tb + u) * E + e] = run;
-            run += h[u];
-          }
-        }
-      }
-    }
-  }
-  gsum[tid] = run;
-  __syncthreads();
-  int gbase = 0, total = 0;
-#pragma unroll
-  for (int gg = 0; gg < kScanGroups; ++gg) {
-    const int v = gsum[gg * kScanExperts + el];
-    gbase += gg < g ? v : 0;
-    total += v;
-  }
-  if (active && g == 0) {
-    counts[e] = min(total, cap);  // kept assignments (capacity factor)
-    if (n_tiles == 0) {           // no rank launch follows: the offsets of an empty batch
-      offsets[e] = 0;
-      if (e == 0) offsets[E] = 0;
-    }
-  }
-  if (active) {
-    if (in_regs) {
-#pragma unroll
-      for (int u = 0; u < kScanRegTiles; ++u)
-        if (t0 + u < t1) ws[(size_t)(t0 + u) * E + e] = pre[u] + gbase;
-    } else {
-      for (int t = t0; t < t1; ++t) ws[(size_t)t * E + e] += gbase;
-    }
-  }
-}
+constexpr int kRankThreads = 1024;  // = kScanThreads: the block scan below is the 1024-thread one
+static_assert(kRankThreads >= MOE_MAX_EXPERTS, "one thread per expert in the offsets scan");
 
-__global__ __launch_bounds__(kWave) void permute_rank_kernel(const int32_t* __restrict__ ids,
-                                                             int R, int E, int nbits,
-                                                             const int32_t* __restrict__ ws,
-                                                             const int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ s2f,
-                                                             int32_t* __restrict__ f2s) {
-  extern __shared__ int32_t run[];  // [E] running positions, then [E] end of each expert
-  int32_t* lim = run + E;
-  const int lane = threadIdx.x;
-  const int32_t* bases = ws + (size_t)blockIdx.x * E;
-  for (int e = lane; e < E; e += kWave) {
-    run[e] = bases[e];  // relative to the expert's first row
-    lim[e] = counts[e];
-  }
-  // One wavefront per workgroup: its LDS accesses take effect in program order, so no barrier
-  // is needed between LDS writes and later reads, nor between a chunk's reads of the running
-  // positions and their update (a workgroup barrier would also wait for this wave's global
-  // stores of the index maps, once per chunk). The wave barriers only keep the compiler from
-  // moving LDS accesses across them.
-  __builtin_amdgcn_wave_barrier();
-  // offsets: exclusive scan of the kept counts, lane l taking experts l*epl .. +epl-1
-  {
-    const int epl = (E + kWave - 1) / kWave;
-    const int e0 = min(lane * epl, E), e1 = min(e0 + epl, E);
-    int sum = 0;
-    for (int e = e0; e < e1; ++e) sum += lim[e];
-    int incl = sum;
+// One workgroup per tile t. Thread (q, e) sums expert e's histogram entries over slice q of the
+// tiles (all of them, and those before t), loads issued 16 at a time; the slices are added in
+// LDS in a fixed order.
+__global__ __launch_bounds__(kRankThreads) void permute_rank_kernel(const int32_t* __restrict__ ids,
+                                                                    int R, int E, int nbits, int cap,
+                                                                    const int32_t* __restrict__ hist,
+                                                                    int n_tiles,
+                                                                    int32_t* __restrict__ counts,
+                                                                    int32_t* __restrict__ offsets,
+                                                                    int32_t* __restrict__ s2f,
+                                                                    int32_t* __restrict__ f2s) {
+  __shared__ int32_t pre_s[kRankThreads], tot_s[kRankThreads];
+  __shared__ int32_t run[MOE_MAX_EXPERTS], lim[MOE_MAX_EXPERTS];
+  __shared__ int32_t wave_sum[kRankThreads / kWave];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;  // <= 1024
+  const int Q = kRankThreads / Ep;
+  const int e = tid % Ep, q = tid / Ep;
+  const int tpq = (n_tiles + Q - 1) / Q;
+  const int t0 = min(q * tpq, n_tiles), t1 = min(t0 + tpq, n_tiles);
+  int pre = 0, tot = 0;
+  if (e < E) {
+    constexpr int B = 16;
+    for (int tb = t0; tb < t1; tb += B) {
+      int h[B];
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
+      for (int u = 0; u < B; ++u) h[u] = tb + u < t1 ? hist[(size_t)(tb + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        tot += h[u];
+        pre += tb + u < t ? h[u] : 0;
+      }
     }
-    int o = incl - sum;
-    for (int e = e0; e < e1; ++e) {
-      const int c = lim[e];
-      if (blockIdx.x == 0) offsets[e] = o;
-      run[e] += o;
-      lim[e] = o + c;  // positions at or past it are beyond the capacity
-      o += c;
-    }
-    if (blockIdx.x == 0 && lane == kWave - 1) offsets[E] = incl;
   }
-  __builtin_amdgcn_wave_barrier();
-  const int base = blockIdx.x * kPermuteTile;
+  pre_s[tid] = pre;
+  tot_s[tid] = tot;
+  __syncthreads();
+  int kept = 0, base = 0;
+  if (tid < E) {
+    int tt = 0;
+    for (int qq = 0; qq < Q; ++qq) {
+      tt += tot_s[qq * Ep + tid];
+      base += pre_s[qq * Ep + tid];
+    }
+    kept = min(tt, cap);  // kept assignments (capacity factor)
+  }
+  const int incl = block_inclusive_scan_1024(kept, wave_sum);
+  if (tid < E) {
+    const int o = incl - kept;  // the expert's first row
+    run[tid] = o + base;        // this tile's first position inside the expert
+    lim[tid] = o + kept;        // positions at or past it are beyond the capacity
+    if (t == 0) {
+      counts[tid] = kept;
+      offsets[tid] = o;
+      if (tid == E - 1) offsets[E] = incl;
+    }
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  // One wavefront walks the tile: its LDS accesses take effect in program order, so no barrier is
+  // needed between a chunk's reads of the running positions and their update; the wave barriers
+  // only keep the compiler from moving LDS accesses across them.
+  const int lane = tid;
+  const int base_i = t * kPermuteTile;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   // the tile's expert ids, all loaded before the walk (one memory latency, not one per chunk):
   // buffer loads through a descriptor that ends at the batch's last entry read zeros past it,
   // so the loads carry no condition that the compiler could turn into a branch around each
   const __amdgpu_buffer_rsrc_t tile_ids = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(ids + base), (short)0, (int)(min(R - base, kPermuteTile) * 4), kRawBufferWord3);
+      (void*)(ids + base_i), (short)0, (int)(min(R - base_i, kPermuteTile) * 4), kRawBufferWord3);
   constexpr int kChunks = kPermuteTile / kWave;
   int key[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) key[c] = clamp_expert(load_tile_id(tile_ids, c * kWave + lane), E);
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int cc = 0; cc < kChunks; ++cc) {
-    const int c = cc * kWave;
-    const int i = base + c + lane;
+    const int i = base_i + cc * kWave + lane;
     const bool valid = i < R;
-    const int e = key[cc];
+    const int ek = key[cc];
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
+      const bool bit = (ek >> b) & 1;
       const uint64_t ones = __ballot(bit);
       same &= bit ? ones : ~ones;
     }
     if (valid) {
       // positions at or past the expert's end are beyond its capacity: dropped
-      const int pos = run[e] + __popcll(same & lower);
-      if (pos < lim[e]) s2f[pos] = i;
-      f2s[i] = pos < lim[e] ? pos : -1;
+      const int pos = run[ek] + __popcll(same & lower);
+      if (pos < lim[ek]) s2f[pos] = i;
+      f2s[i] = pos < lim[ek] ? pos : -1;
     }
     __builtin_amdgcn_wave_barrier();
-    // the highest lane of each group of equal experts advances that expert's base
-    if (valid && (63 - __clzll(same)) == lane) run[e] += __popcll(same);
+    // the highest lane of each group of equal experts advances that expert's position
+    if (valid && (63 - __clzll(same)) == lane) run[ek] += __popcll(same);
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -405,17 +357,15 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
                                                    flat_to_sorted, static_cast<uint4*>(x_sorted));
     return hipGetLastError();
   }
-  if (n_tiles > 0) {
-    permute_hist_kernel<<<n_tiles, 256, lds, stream>>>(ids, R, E, ws);
-    hipError_t st = hipGetLastError();
-    if (st != hipSuccess) return st;
+  if (n_tiles == 0) {  // an empty batch: no rows, every expert's count and offset is zero
+    hipError_t st = launch_fill_i32(counts, E, 0, stream);
+    return st == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, stream) : st;
   }
-  permute_scan_kernel<<<(E + kScanExperts - 1) / kScanExperts, kScanWgThreads, 0, stream>>>(
-      ws, n_tiles, E, cap, counts, offsets);
+  permute_hist_kernel<<<n_tiles, 256, lds, stream>>>(ids, R, E, ws);
   hipError_t st = hipGetLastError();
-  if (st != hipSuccess || n_tiles == 0) return st;
-  permute_rank_kernel<<<n_tiles, kWave, 2 * lds, stream>>>(ids, R, E, nbits, ws, counts, offsets,
-                                                            sorted_to_flat, flat_to_sorted);
+  if (st != hipSuccess) return st;
+  permute_rank_kernel<<<n_tiles, kRankThreads, 0, stream>>>(ids, R, E, nbits, cap, ws, n_tiles, counts,
+                                                             offsets, sorted_to_flat, flat_to_sorted);
   st = hipGetLastError();
   if (st != hipSuccess) return st;
   permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,

@@ -416,6 +416,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--zipf", type=float, default=None,
+                    help="override the workload's Zipf logit-bias exponent (0 = no bias), for "
+                         "robustness runs of the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--capacity-sweep", action="store_true",
@@ -454,6 +457,9 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.config]
+    if args.zipf is not None:
+        cfg = cfg.with_(zipf_s=args.zipf if args.zipf > 0 else None,
+                        note=f"{cfg.note}, logit bias Zipf s={args.zipf}")
     T, E, k, d, d_ff = cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff
     act_t = torch.float32 if cfg.act == "f32" else torch.bfloat16
     w_t = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3fn": torch.float8_e4m3fn}[cfg.w]

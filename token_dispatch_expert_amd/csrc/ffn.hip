@@ -32,6 +32,7 @@
 // added to the running sum times the block's scale.
 #include <math.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "moe_internal.h"
@@ -848,13 +849,21 @@ __device__ __forceinline__ void tile_epilogue_impl(const TiledArgs& p, const f32
 // round's tiles that way. MODE 2 (a second launch) adds a tile's S partials in chunk order and
 // applies the epilogue, so the result does not depend on timing and needs no synchronisation
 // inside a launch.
+// HYB (the large prefill tiles): an expert's rows are dealt to its row tiles in whole 16-row
+// fragments as evenly as the tile count allows (300 rows: two tiles of 10 and 9 fragments, not
+// 256 + 44), so that the row tiles of one column block, which run side by side on one XCD and
+// read the same weights, take about the same time; and each wave runs a body compiled for the
+// number of its 16-row fragments that hold rows (absent ones take no LDS reads and no MFMAs),
+// so a partial tile costs what its fragments need while every body keeps a branch-free inner
+// loop.
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
-          bool ASKIP = false, int MODE = 0>
+          bool ASKIP = false, int MODE = 0, bool HYB = false>
 __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem, int rank,
                                          int nranks, int min_rows, int max_rows) {
   static_assert(DK == 64 || DK == 128, "contraction step: an even number of 32-wide slices");
   static_assert(WF == kBF16 || (WF == kFP8 && DK >= 64), "weight format");
   static_assert(MODE == 0 || !ASKIP, "contraction split: every row loaded");
+  static_assert(!HYB || !ASKIP, "row skipping is chosen per tile");
   static_assert(MODE != 1 || (WF == kBF16 && WGM * WM * WGN * WN <= kSplitTileElems),
                 "decode contraction split: bf16 weights, tiles of at most 64 x 128");
   constexpr bool F8 = WF == kFP8;
@@ -884,7 +893,11 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool loads_a = AI >= NW || wave < AI;  // wave-uniform
-  const int wm = wave % WGM, wn = wave / WGM;
+  // HYB: waves w and w + 4 share a SIMD (the hardware deals a workgroup's waves to the four
+  // SIMDs in turn), so wave w takes the row block w / WGN: with two row blocks the two waves of a
+  // SIMD own different halves of the tile, and a tile whose rows fill only the upper half still
+  // keeps every SIMD busy with half the work.
+  const int wm = HYB ? wave / WGN : wave % WGM, wn = HYB ? wave % WGN : wave / WGM;
   constexpr int cols_per_tile = GATED ? TN / 2 : TN;
   const int NT = (p.N + cols_per_tile - 1) / cols_per_tile;
   build_item_prefix(pre, scan_tmp, p.offsets, p.E, p.rows, max_rows, NT, offs, min_rows, TM);
@@ -914,8 +927,17 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
     const int j = local - g * kGroupM * NT;
     const int nt = j / gm;
     const int mt = g * kGroupM + j % gm;
-    r0 = ebeg + mt * TM;
-    nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
+    if constexpr (HYB) {
+      // fragments dealt evenly: the first fr % MT tiles take one more (at most TM / 16 each,
+      // at least one, since MT = ceil(n / TM)); the ragged last fragment ends the last tile
+      const int fr = (__builtin_amdgcn_readfirstlane(offs[e + 1]) - ebeg + 15) / 16;
+      const int q = fr / MT, rem = fr - q * MT;
+      r0 = ebeg + 16 * (mt * q + min(mt, rem));
+      nrows = min(16 * (q + (mt < rem ? 1 : 0)), __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
+    } else {
+      r0 = ebeg + mt * TM;
+      nrows = min(TM, __builtin_amdgcn_readfirstlane(offs[e + 1]) - r0);
+    }
     c0 = nt * cols_per_tile;
   };
 
@@ -1001,257 +1023,278 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
     const int st_lo = split ? chunk * nst / S : 0, st_hi = split ? (chunk + 1) * nst / S : nst;
     int e, r0, nrows, c0;
     tile_of(item, e, r0, nrows, c0);
-    // Weight tiles of an expert whose rows fit one row tile are read exactly once: in the decode
-    // tiles and the streaming role they load with the non-temporal policy, so they leave the
-    // L2 first and the weights of experts with several row tiles stay there for their re-reads
-    // (c2 FFN -7%, c3 -6.5%). The large prefill tiles keep the default policy (+3.8% at c4 with
-    // the same rule).
-    const bool b_once = (ASKIP || MODE == 0 || MODE == 1) &&
-                        __builtin_amdgcn_readfirstlane(offs[e + 1]) -
-                                __builtin_amdgcn_readfirstlane(offs[e]) <= TM;
-    // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
-    // issued, and the 16-row fragments past it take no LDS reads and no MFMAs: those LDS rows
-    // keep stale data, which could only reach accumulator rows that are never stored (row r of
-    // the product depends on row r of A alone).
-    constexpr int RPI = 64 / CPRA;  // tile rows per A load instruction
-    int aiw = 0;
-#pragma unroll
-    for (int i = 0; i < AIW; ++i)
-      aiw += (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows)) ? 1 : 0;
-    const int lpw = aiw + BIW;  // this wave's loads per step
-
-    // Loads are buffer loads into LDS: a descriptor per operand holds the tile's base and its
-    // byte extent (rows past the expert's last row, or past the last column, read as zeros, so
-    // nothing is clamped), one 32-bit lane offset serves all of a wave's load instructions, and
-    // the per-instruction and per-step parts are wave-uniform scalar offsets. That keeps the
-    // address registers at two, whatever the number of load instructions.
-    // Instruction i of this wave covers tile rows shifted by i * NW * rows-per-instruction; the
-    // XOR swizzle of a row repeats with that period, so the lane's chunk is the same for all i.
-    const uint8_t* Xt = static_cast<const uint8_t*>(p.X) + (size_t)r0 * p.K * 2;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)Xt, (short)0, (int)((unsigned)nrows * (unsigned)p.K * 2u), kBufferWord3);
-    const size_t wcol = (size_t)c0 * p.K * WB;  // the tile's first B row (weight row c0)
-    const size_t bbytes = (size_t)(p.N - c0) * p.K * WB;
-    const unsigned bext = bbytes > 0xffffffffu ? 0xffffffffu : (unsigned)bbytes;
-    const __amdgpu_buffer_rsrc_t rB1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(static_cast<const uint8_t*>(p.W1) + (size_t)e * wstride + wcol), (short)0, (int)bext, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rB2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(static_cast<const uint8_t*>(p.W2) + (size_t)e * wstride + wcol), (short)0, (int)bext, kBufferWord3) : rB1;
-    constexpr int RPA = 64 / CPRA, RPB = 64 / CPRB;  // tile rows per load instruction
-    int a_lane, b_lane;  // byte offsets of instruction 0 (this lane)
-    {
-      const int q = wave * 64 + lane;
-      const int r = q / CPRA, c = dswz<CPRA>(r, q % CPRA) - r * CPRA;  // source chunk (XOR involution)
-      a_lane = (r * p.K * 2) + c * 16;
-    }
-    // B row t of the tile -> weight row offset from c0 (gated tiles interleave gate and up
-    // halves of WN rows per wave block)
-    auto b_row = [&](int t) __attribute__((always_inline)) {
-      return GATED ? (t / WN) * (WN / 2) + (t % WN) % (WN / 2) : t;
-    };
-    {
-      const int q = wave * 64 + lane;
-      const int t = q / CPRB, c = dswz<CPRB>(t, q % CPRB) - t * CPRB;
-      b_lane = b_row(t) * p.K * WB + c * 16;
-    }
-    const int t0w = wave * RPB;  // first B row of this wave's instruction 0 (wave-uniform)
-
-    auto issue = [&](int st) __attribute__((always_inline)) {
-      u32x4* slot = ring + (st % RING) * STAGE;
-      const int ka = st * DK * 2, kb = st * DK * WB;
-#pragma unroll
+    // MFP: this wave's 16-row fragments that hold rows of the tile, fixed at compile time (HYB:
+    // one body per count, so the fragment loop has no branches), or -1: checked at run time
+    // (ASKIP)
+    auto run_tile = [&](auto mfp_tag) __attribute__((always_inline)) {
+      constexpr int MFP = decltype(mfp_tag)::value;
+      auto present = [&](int mf) __attribute__((always_inline)) {
+        return MFP >= 0 ? mf < MFP : !(ASKIP && wm * WM + mf * 16 >= nrows);
+      };
+      // Weight tiles of an expert whose rows fit one row tile are read exactly once: in the decode
+      // tiles and the streaming role they load with the non-temporal policy, so they leave the
+      // L2 first and the weights of experts with several row tiles stay there for their re-reads
+      // (c2 FFN -7%, c3 -6.5%). The large prefill tiles keep the default policy (+3.8% at c4 with
+      // the same rule).
+      const bool b_once = (ASKIP || MODE == 0 || MODE == 1) &&
+                          __builtin_amdgcn_readfirstlane(offs[e + 1]) -
+                                  __builtin_amdgcn_readfirstlane(offs[e]) <= TM;
+      // With ASKIP, A load instructions whose rows all lie past the expert's last row are not
+      // issued (HYB: they are issued out of the descriptor's range, which reads nothing and
+      // keeps the load count fixed), and the 16-row fragments past it take no LDS reads and no
+      // MFMAs: those LDS rows keep stale data or zeros, which could only reach accumulator rows
+      // that are never stored (row r of the product depends on row r of A alone).
+      constexpr int RPI = 64 / CPRA;  // tile rows per A load instruction
+      int aiw = 0;
+  #pragma unroll
       for (int i = 0; i < AIW; ++i)
-        if (loads_a && (!ASKIP || (wave + i * NW) * RPA < nrows))
-          buffer_load_lds16(rA, slot + (wave + i * NW) * 64, a_lane, i * NW * RPA * p.K * 2 + ka);
-#pragma unroll
-      for (int i = 0; i < BIW; ++i) {
-        const int ti = t0w + i * NW * RPB;  // first row of instruction i (wave-uniform)
-        const bool up = GATED && (ti % WN) >= WN / 2;
-        if (b_once)
-          buffer_load_lds16<kNonTemporal>(up ? rB2 : rB1, slot + ACH + (wave + i * NW) * 64, b_lane,
-                                          (b_row(ti) - b_row(t0w)) * p.K * WB + kb);
-        else
-          buffer_load_lds16<0>(up ? rB2 : rB1, slot + ACH + (wave + i * NW) * 64, b_lane,
-                               (b_row(ti) - b_row(t0w)) * p.K * WB + kb);
-      }
-    };
+        aiw += (loads_a && (!ASKIP || (wave + i * NW) * RPI < nrows)) ? 1 : 0;
+      const int lpw = aiw + BIW;  // this wave's loads per step
 
-    f32x4 acc[MF][NF];
-    f32x4 part[F8 ? MF : 1][F8 ? NF : 1];  // fp8: this scale block's sums
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int jj = 0; jj < NF; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (F8) {
-#pragma unroll
+      // Loads are buffer loads into LDS: a descriptor per operand holds the tile's base and its
+      // byte extent (rows past the expert's last row, or past the last column, read as zeros, so
+      // nothing is clamped), one 32-bit lane offset serves all of a wave's load instructions, and
+      // the per-instruction and per-step parts are wave-uniform scalar offsets. That keeps the
+      // address registers at two, whatever the number of load instructions.
+      // Instruction i of this wave covers tile rows shifted by i * NW * rows-per-instruction; the
+      // XOR swizzle of a row repeats with that period, so the lane's chunk is the same for all i.
+      const uint8_t* Xt = static_cast<const uint8_t*>(p.X) + (size_t)r0 * p.K * 2;
+      const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)Xt, (short)0, (int)((unsigned)nrows * (unsigned)p.K * 2u), kBufferWord3);
+      const size_t wcol = (size_t)c0 * p.K * WB;  // the tile's first B row (weight row c0)
+      const size_t bbytes = (size_t)(p.N - c0) * p.K * WB;
+      const unsigned bext = bbytes > 0xffffffffu ? 0xffffffffu : (unsigned)bbytes;
+      const __amdgpu_buffer_rsrc_t rB1 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(static_cast<const uint8_t*>(p.W1) + (size_t)e * wstride + wcol), (short)0, (int)bext, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rB2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(static_cast<const uint8_t*>(p.W2) + (size_t)e * wstride + wcol), (short)0, (int)bext, kBufferWord3) : rB1;
+      constexpr int RPA = 64 / CPRA, RPB = 64 / CPRB;  // tile rows per load instruction
+      int a_lane, b_lane;  // byte offsets of instruction 0 (this lane)
+      {
+        const int q = wave * 64 + lane;
+        const int r = q / CPRA, c = dswz<CPRA>(r, q % CPRA) - r * CPRA;  // source chunk (XOR involution)
+        a_lane = (r * p.K * 2) + c * 16;
+      }
+      // B row t of the tile -> weight row offset from c0 (gated tiles interleave gate and up
+      // halves of WN rows per wave block)
+      auto b_row = [&](int t) __attribute__((always_inline)) {
+        return GATED ? (t / WN) * (WN / 2) + (t % WN) % (WN / 2) : t;
+      };
+      {
+        const int q = wave * 64 + lane;
+        const int t = q / CPRB, c = dswz<CPRB>(t, q % CPRB) - t * CPRB;
+        b_lane = b_row(t) * p.K * WB + c * 16;
+      }
+      const int t0w = wave * RPB;  // first B row of this wave's instruction 0 (wave-uniform)
+
+      auto issue = [&](int st) __attribute__((always_inline)) {
+        u32x4* slot = ring + (st % RING) * STAGE;
+        const int ka = st * DK * 2, kb = st * DK * WB;
+  #pragma unroll
+        for (int i = 0; i < AIW; ++i)
+          if (loads_a && (!ASKIP || (wave + i * NW) * RPA < nrows))
+            buffer_load_lds16(rA, slot + (wave + i * NW) * 64, a_lane,
+                              (HYB && (wave + i * NW) * RPA >= nrows) ? 0x40000000
+                                                                      : i * NW * RPA * p.K * 2 + ka);
+  #pragma unroll
+        for (int i = 0; i < BIW; ++i) {
+          const int ti = t0w + i * NW * RPB;  // first row of instruction i (wave-uniform)
+          const bool up = GATED && (ti % WN) >= WN / 2;
+          if (b_once)
+            buffer_load_lds16<kNonTemporal>(up ? rB2 : rB1, slot + ACH + (wave + i * NW) * 64, b_lane,
+                                            (b_row(ti) - b_row(t0w)) * p.K * WB + kb);
+          else
+            buffer_load_lds16<0>(up ? rB2 : rB1, slot + ACH + (wave + i * NW) * 64, b_lane,
+                                 (b_row(ti) - b_row(t0w)) * p.K * WB + kb);
+        }
+      };
+
+      f32x4 acc[MF][NF];
+      f32x4 part[F8 ? MF : 1][F8 ? NF : 1];  // fp8: this scale block's sums
+  #pragma unroll
       for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int jj = 0; jj < NF; ++jj) part[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // fp8: stage the scale rows of every wave column block (gate and up halves for the gated
-    // GEMM) in LDS; nothing is in flight here, the previous item ended with a full drain
-    if constexpr (F8) {
-      for (int idx = tid; idx < WGN * 2 * KBn; idx += NTH) {
-        const int blk = idx / (2 * KBn), half = (idx / KBn) & 1, kb = idx % KBn;
-        const int n0 = GATED ? c0 + blk * (WN / 2) : c0 + blk * WN;
-        const size_t srow = ((size_t)e * NB + min(n0 / 128, NB - 1)) * KBn + kb;
-        sc_lds[idx] = (GATED && half) ? p.S2[srow] : (half ? 0.f : p.S1[srow]);
+  #pragma unroll
+        for (int jj = 0; jj < NF; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (F8) {
+  #pragma unroll
+        for (int i = 0; i < MF; ++i)
+  #pragma unroll
+          for (int jj = 0; jj < NF; ++jj) part[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      __syncthreads();
-    }
+      // fp8: stage the scale rows of every wave column block (gate and up halves for the gated
+      // GEMM) in LDS; nothing is in flight here, the previous item ended with a full drain
+      if constexpr (F8) {
+        for (int idx = tid; idx < WGN * 2 * KBn; idx += NTH) {
+          const int blk = idx / (2 * KBn), half = (idx / KBn) & 1, kb = idx % KBn;
+          const int n0 = GATED ? c0 + blk * (WN / 2) : c0 + blk * WN;
+          const size_t srow = ((size_t)e * NB + min(n0 / 128, NB - 1)) * KBn + kb;
+          sc_lds[idx] = (GATED && half) ? p.S2[srow] : (half ? 0.f : p.S1[srow]);
+        }
+        __syncthreads();
+      }
 
-    // Software pipeline over 32-wide contraction slices: the fragments of the next slice are read
-    // from LDS while the MFMAs of the current one run (B fragments into the other of two
-    // register sets, A fragment mf right after its last MFMA of the current slice), so the MFMA
-    // pipe never waits for a fresh read. The barrier that hands a step's slot back sits before
-    // the MFMAs of the step's last slice, whose fragments are already in registers.
-    constexpr int NS = DK / 32;  // slices per step (even)
-    // k order inside a step. bf16: slice h, lane L holds k = 32h + 8(L/16) .. +7 (16-byte chunk
-    // 4h + L/16 of the A and B rows). fp8: a B chunk of 16 bytes holds 16 k, so a lane reads
-    // chunk 4j + L/16 of its B row once for the slice pair (2j, 2j+1), its bytes 0-7 in slice 2j
-    // and 8-15 in slice 2j+1, and A follows the same k (bf16 chunks 8j + 2(L/16) + {0, 1}). Any
-    // k order is the same contraction as long as A and B agree.
-    auto read_a = [&](const u32x4* slot, int h, int mf, bf16x8& dst) __attribute__((always_inline)) {
-      const int c = F8 ? (h >> 1) * 8 + (lane >> 4) * 2 + (h & 1) : h * 4 + (lane >> 4);
-      const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
-      __builtin_memcpy(&dst, &v, 16);
-    };
-    // B chunk of 16-row fragment nf: bf16, the chunk of slice h; fp8, the chunk of slice pair h/2
-    auto read_b = [&](const u32x4* slot, int h, int nf, u32x4& dst) __attribute__((always_inline)) {
-      const int c = F8 ? (h >> 1) * 4 + (lane >> 4) : h * 4 + (lane >> 4);
-      dst = slot[ACH + dswz<CPRB>(wn * WN + nf * 16 + (lane & 15), c)];
-    };
-    auto bar = [&]() __attribute__((always_inline)) {
-      // A bare s_barrier: a fence here would make the compiler drain all outstanding
-      // direct-to-LDS loads. The signal fences only stop the compiler from moving LDS accesses
-      // across the barrier.
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    };
-    bf16x8 afr[MF];
-    // B chunks: bf16, those of the current slice and of the next; fp8, one set (a slice pair's)
-    u32x4 bq[F8 ? 1 : 2][NF];
-    // the whole ring is free (the previous item ended with a barrier after its last reads)
-#pragma unroll
-    for (int r = 0; r < RING; ++r)
-      if (st_lo + r < st_hi) issue(st_lo + r);
-    // this wave's loads of the first step are done once at most the later steps' are pending
-    wait_vmcnt_dyn<(RING - 1) * LPW>(min(RING - 1, st_hi - 1 - st_lo) * lpw);
-    bar();
-    {
-      const u32x4* slot = ring + (st_lo % RING) * STAGE;
-#pragma unroll
-      for (int nf = 0; nf < NF; ++nf) read_b(slot, 0, nf, bq[0][nf]);
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
-        if (!(ASKIP && wm * WM + mf * 16 >= nrows)) read_a(slot, 0, mf, afr[mf]);
-    }
-    for (int st = st_lo; st < st_hi; ++st) {
-      const u32x4* slot = ring + (st % RING) * STAGE;
-      const u32x4* nslot = ring + ((st + 1) % RING) * STAGE;
-      static_for<NS>([&](auto hc) __attribute__((always_inline)) {
-        constexpr int h = decltype(hc)::value;
-        constexpr int P = h & 1;  // B register set of this slice (bf16)
-        // The next slice is read whether or not it exists: past the item's last step the reads
-        // land in registers that are never used (in-bounds LDS, no loads in flight), which keeps
-        // the code free of branches and the compiler's read counts exact.
-        if (h == NS - 1) {
-          wait_lgkmcnt0();  // this wave's reads of step st are back
-          if (st + 1 < st_hi) {
-            // the next slice opens step st+1: this wave's loads of it have landed (at most the
-            // later steps' are pending), and after the barrier both hold for every wave, so
-            // step st's slot takes step st+RING
-            wait_vmcnt_dyn<(RING - 2) * LPW>(min(RING - 2, st_hi - 2 - st) * lpw);
-            bar();
-            if (st + RING < st_hi) issue(st + RING);
-          }
-        }
-        // fp8: the wave issuing a slice's conversions, MFMAs and reads runs at raised priority, so
-        // the SIMD's other wave, in its barrier or load issue, does not hold it back (c5 FFN -2%;
-        // bf16 tiles measured 0.5% slower with it)
-        if constexpr (F8) __builtin_amdgcn_s_setprio(1);
-        const u32x4* rs = h + 1 < NS ? slot : nslot;
-        const int rh = (h + 1) % NS;
-        bf16x8 bfr[NF];
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf) {
-          if constexpr (F8) {
-            const u32x4 v = bq[0][nf];
-            bfr[nf] = fp8x8_to_bf16((h & 1) ? make_uint2(v[2], v[3]) : make_uint2(v[0], v[1]));
-          } else {
-            __builtin_memcpy(&bfr[nf], &bq[P][nf], 16);
-          }
-        }
-        // next B chunks: bf16 every slice (into the other set); fp8 after the second slice of a
-        // pair has been widened (into the same set)
-        constexpr int NBR = F8 ? ((h & 1) ? NF : 0) : NF;
-        if constexpr (NBR > 0) {
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf) read_b(rs, rh, nf, bq[F8 ? 0 : P ^ 1][nf]);
-        }
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) {
-          if (ASKIP && wm * WM + mf * 16 >= nrows) continue;  // wave-uniform: absent rows
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            if constexpr (F8)
-              part[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], part[mf][nf], 0, 0, 0);
-            else
-              acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
-          }
-          read_a(rs, rh, mf, afr[mf]);
-        }
-        // instruction order of the slice: the B reads, then per 16-row fragment its MFMAs and
-        // the read of its next A fragment
-        if constexpr (NBR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NBR, 0);
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) {
-          __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        // the reads stay in this slice (not sunk to their first use)
+      // Software pipeline over 32-wide contraction slices: the fragments of the next slice are read
+      // from LDS while the MFMAs of the current one run (B fragments into the other of two
+      // register sets, A fragment mf right after its last MFMA of the current slice), so the MFMA
+      // pipe never waits for a fresh read. The barrier that hands a step's slot back sits before
+      // the MFMAs of the step's last slice, whose fragments are already in registers.
+      constexpr int NS = DK / 32;  // slices per step (even)
+      // k order inside a step. bf16: slice h, lane L holds k = 32h + 8(L/16) .. +7 (16-byte chunk
+      // 4h + L/16 of the A and B rows). fp8: a B chunk of 16 bytes holds 16 k, so a lane reads
+      // chunk 4j + L/16 of its B row once for the slice pair (2j, 2j+1), its bytes 0-7 in slice 2j
+      // and 8-15 in slice 2j+1, and A follows the same k (bf16 chunks 8j + 2(L/16) + {0, 1}). Any
+      // k order is the same contraction as long as A and B agree.
+      auto read_a = [&](const u32x4* slot, int h, int mf, bf16x8& dst) __attribute__((always_inline)) {
+        const int c = F8 ? (h >> 1) * 8 + (lane >> 4) * 2 + (h & 1) : h * 4 + (lane >> 4);
+        const u32x4 v = slot[dswz<CPRA>(wm * WM + mf * 16 + (lane & 15), c)];
+        __builtin_memcpy(&dst, &v, 16);
+      };
+      // B chunk of 16-row fragment nf: bf16, the chunk of slice h; fp8, the chunk of slice pair h/2
+      auto read_b = [&](const u32x4* slot, int h, int nf, u32x4& dst) __attribute__((always_inline)) {
+        const int c = F8 ? (h >> 1) * 4 + (lane >> 4) : h * 4 + (lane >> 4);
+        dst = slot[ACH + dswz<CPRB>(wn * WN + nf * 16 + (lane & 15), c)];
+      };
+      auto bar = [&]() __attribute__((always_inline)) {
+        // A bare s_barrier: a fence here would make the compiler drain all outstanding
+        // direct-to-LDS loads. The signal fences only stop the compiler from moving LDS accesses
+        // across the barrier.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if constexpr (F8) __builtin_amdgcn_s_setprio(0);
-        if constexpr (F8) {
-          if (h == NS - 1 && (st + 1) % KBS == 0) {  // end of a 128-long scale block
-            const int kb = st / KBS;
-            const float s0 = sc_lds[(wn * 2) * KBn + kb];
-            const float s1 = GATED ? sc_lds[(wn * 2 + 1) * KBn + kb] : s0;
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-              for (int nf = 0; nf < NF; ++nf) {
-                const float sc = (GATED && nf >= NF / 2) ? s1 : s0;
-                acc[mf][nf] += sc * part[mf][nf];
-                part[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
-              }
-          }
-        }
-      });
-    }
-    __syncthreads();  // all waves done reading the ring before the next item refills it
-    if (MODE == 1 || (MODE == 3 && split)) {
-      float* mine = p.partial + ((size_t)(item - first_split) * S + chunk) * kSlot;
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        if (wm * WM + mf * 16 >= nrows) continue;  // absent rows: nothing to keep
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-          *reinterpret_cast<f32x4*>(mine + ((mf * NF + nf) * NTH + tid) * 4) = acc[mf][nf];
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      };
+      bf16x8 afr[MF];
+      // B chunks: bf16, those of the current slice and of the next; fp8, one set (a slice pair's)
+      u32x4 bq[F8 ? 1 : 2][NF];
+      // the whole ring is free (the previous item ended with a barrier after its last reads)
+  #pragma unroll
+      for (int r = 0; r < RING; ++r)
+        if (st_lo + r < st_hi) issue(st_lo + r);
+      // this wave's loads of the first step are done once at most the later steps' are pending
+      wait_vmcnt_dyn<(RING - 1) * LPW>(min(RING - 1, st_hi - 1 - st_lo) * lpw);
+      bar();
+      {
+        const u32x4* slot = ring + (st_lo % RING) * STAGE;
+  #pragma unroll
+        for (int nf = 0; nf < NF; ++nf) read_b(slot, 0, nf, bq[0][nf]);
+  #pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+          if (present(mf)) read_a(slot, 0, mf, afr[mf]);
       }
+      for (int st = st_lo; st < st_hi; ++st) {
+        const u32x4* slot = ring + (st % RING) * STAGE;
+        const u32x4* nslot = ring + ((st + 1) % RING) * STAGE;
+        static_for<NS>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int h = decltype(hc)::value;
+          constexpr int P = h & 1;  // B register set of this slice (bf16)
+          // The next slice is read whether or not it exists: past the item's last step the reads
+          // land in registers that are never used (in-bounds LDS, no loads in flight), which keeps
+          // the code free of branches and the compiler's read counts exact.
+          if (h == NS - 1) {
+            wait_lgkmcnt0();  // this wave's reads of step st are back
+            if (st + 1 < st_hi) {
+              // the next slice opens step st+1: this wave's loads of it have landed (at most the
+              // later steps' are pending), and after the barrier both hold for every wave, so
+              // step st's slot takes step st+RING
+              wait_vmcnt_dyn<(RING - 2) * LPW>(min(RING - 2, st_hi - 2 - st) * lpw);
+              bar();
+              if (st + RING < st_hi) issue(st + RING);
+            }
+          }
+          // fp8: the wave issuing a slice's conversions, MFMAs and reads runs at raised priority, so
+          // the SIMD's other wave, in its barrier or load issue, does not hold it back (c5 FFN -2%;
+          // bf16 tiles measured 0.5% slower with it)
+          if constexpr (F8) __builtin_amdgcn_s_setprio(1);
+          const u32x4* rs = h + 1 < NS ? slot : nslot;
+          const int rh = (h + 1) % NS;
+          bf16x8 bfr[NF];
+  #pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            if constexpr (F8) {
+              const u32x4 v = bq[0][nf];
+              bfr[nf] = fp8x8_to_bf16((h & 1) ? make_uint2(v[2], v[3]) : make_uint2(v[0], v[1]));
+            } else {
+              __builtin_memcpy(&bfr[nf], &bq[P][nf], 16);
+            }
+          }
+          // next B chunks: bf16 every slice (into the other set); fp8 after the second slice of a
+          // pair has been widened (into the same set)
+          constexpr int NBR = F8 ? ((h & 1) ? NF : 0) : NF;
+          if constexpr (NBR > 0 && MFP != 0) {
+  #pragma unroll
+            for (int nf = 0; nf < NF; ++nf) read_b(rs, rh, nf, bq[F8 ? 0 : P ^ 1][nf]);
+          }
+  #pragma unroll
+          for (int mf = 0; mf < MF; ++mf) {
+            if (!present(mf)) continue;  // wave-uniform: absent rows
+  #pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+              if constexpr (F8)
+                part[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], part[mf][nf], 0, 0, 0);
+              else
+                acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+            }
+            read_a(rs, rh, mf, afr[mf]);
+          }
+          // instruction order of the slice: the B reads, then per 16-row fragment its MFMAs and
+          // the read of its next A fragment
+          if constexpr (NBR > 0 && MFP != 0) __builtin_amdgcn_sched_group_barrier(0x100, NBR, 0);
+  #pragma unroll
+          for (int mf = 0; mf < (MFP >= 0 ? MFP : MF); ++mf) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          // the reads stay in this slice (not sunk to their first use)
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if constexpr (F8) __builtin_amdgcn_s_setprio(0);
+          if constexpr (F8) {
+            if (h == NS - 1 && (st + 1) % KBS == 0) {  // end of a 128-long scale block
+              const int kb = st / KBS;
+              const float s0 = sc_lds[(wn * 2) * KBn + kb];
+              const float s1 = GATED ? sc_lds[(wn * 2 + 1) * KBn + kb] : s0;
+  #pragma unroll
+              for (int mf = 0; mf < MF; ++mf)
+  #pragma unroll
+                for (int nf = 0; nf < NF; ++nf) {
+                  const float sc = (GATED && nf >= NF / 2) ? s1 : s0;
+                  acc[mf][nf] += sc * part[mf][nf];
+                  part[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+          }
+        });
+      }
+      __syncthreads();  // all waves done reading the ring before the next item refills it
+      if (MODE == 1 || (MODE == 3 && split)) {
+        float* mine = p.partial + ((size_t)(item - first_split) * S + chunk) * kSlot;
+  #pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+          if (wm * WM + mf * 16 >= nrows) continue;  // absent rows: nothing to keep
+  #pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            *reinterpret_cast<f32x4*>(mine + ((mf * NF + nf) * NTH + tid) * 4) = acc[mf][nf];
+        }
+      } else {
+        tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0);
+      }
+    };
+    if constexpr (HYB) {
+      // this wave's present fragments (wave-uniform), one body per count
+      const int nfw = __builtin_amdgcn_readfirstlane(min(MF, max(0, (nrows - wm * WM + 15) / 16)));
+      static_for<MF + 1>([&](auto c) __attribute__((always_inline)) {
+        if (nfw == decltype(c)::value) run_tile(std::integral_constant<int, decltype(c)::value>{});
+      });
     } else {
-      tile_epilogue(p, acc, wm, wn, lane, r0, nrows, c0);
+      run_tile(std::integral_constant<int, ASKIP ? -1 : MF>{});
     }
   }
 }
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
-          bool ASKIP = false, int MODE = 0>
+          bool ASKIP = false, int MODE = 0, bool HYB = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void ffn_tiled_dl_kernel(TiledArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  dl_tiles<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP, MODE>(p, smem, blockIdx.x, gridDim.x,
-                                                               p.min_rows, 0x7fffffff);
+  dl_tiles<WF, GATED, WM, WN, WGM, WGN, RING, DK, ASKIP, MODE, HYB>(p, smem, blockIdx.x, gridDim.x,
+                                                                    p.min_rows, 0x7fffffff);
 }
 
 // LDS bytes of dl_tiles for a tile shape (prefix arrays, ring, fp8 scale rows)
@@ -1328,8 +1371,8 @@ __global__ __launch_bounds__(512) void ffn_prefill_kernel(TiledArgs p) {
   if ((int)blockIdx.x < X)
     dl_tiles<WF, GATED, 16, CWN, 1, 8, CRING, CDK, true>(p, smem, blockIdx.x, X, 0, kStreamMaxRows);
   else
-    dl_tiles<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 3>(p, smem, blockIdx.x - X, G - X,
-                                                              kStreamMaxRows, 0x7fffffff);
+    dl_tiles<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 3, true>(p, smem, blockIdx.x - X, G - X,
+                                                                    kStreamMaxRows, 0x7fffffff);
 }
 
 template <int WF, bool GATED, int HWM, int HWN, int HRING, int HDK, int CWN, int CRING, int CDK>
@@ -1349,7 +1392,7 @@ static hipError_t launch_prefill(const TiledArgs& p, const DeviceInfo& dev, hipS
   TiledArgs q = p;
   q.min_rows = kStreamMaxRows;
   const size_t lds2 = ((size_t)(p.E + 1 + 3) / 4 * 4 * 2 + 512) * sizeof(int32_t);
-  ffn_tiled_dl_kernel<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 2><<<dev.num_cus, 512, lds2, stream>>>(q);
+  ffn_tiled_dl_kernel<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 2, true><<<dev.num_cus, 512, lds2, stream>>>(q);
   return hipGetLastError();
 }
 

@@ -181,6 +181,22 @@ def test_row_counts_at_tile_boundaries(dev, act, w):
     assert got["counts"].tolist() == counts
 
 
+@pytest.mark.parametrize("w,d,d_ff", [("bf16", 128, 192), ("fp8_e4m3fn", 256, 384)])
+def test_prefill_fragment_counts(dev, w, d, d_ff):
+    # the large prefill tiles deal an expert's rows to its row tiles in whole 16-row fragments
+    # and each wave runs a body compiled for the fragments of its row half that hold rows: these
+    # counts (21, 37, ..., 245 rows, and experts of 300-1000 rows over 2-4 tiles) reach every
+    # count in both halves of the 256-row bf16 and 128-row fp8 tiles
+    counts = [16 * j + 5 for j in range(1, 16)] + [300, 520, 777, 1000]
+    E = len(counts)
+    owners = [[e] for e, c in enumerate(counts) for _ in range(c)]
+    np.random.default_rng(8).shuffle(owners)
+    cfg = synth.tiny_config(T=len(owners), d=d, E=E, k=1, d_ff=d_ff, act="bf16", w=w, seed=8)
+    assert cfg.T * cfg.k >= 32 * cfg.E  # the prefill launch
+    got, _ = run_full(cfg, dev, logits=_onehot_logits(owners, E))
+    assert got["counts"].tolist() == counts
+
+
 @pytest.mark.parametrize("act,w,d,d_ff", [("bf16", "bf16", 136, 200), ("f32", "f32", 40, 24),
                                            ("bf16", "bf16", 8, 8)])
 def test_dims_not_multiples_of_tiles(dev, act, w, d, d_ff):

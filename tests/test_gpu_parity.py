@@ -390,6 +390,8 @@ def test_decode_few_experts_long_contraction(dev, T, E, k):
     (200, 256, 6, 3, 384, "bf16", "bf16", 1.2),        # prefill, every tile in a split last round
     (300, 384, 5, 2, 640, "bf16", "bf16", None),       # prefill, last round split in 3
     (700, 512, 8, 2, 512, "bf16", "fp8_e4m3fn", 1.0),  # fp8 prefill, last round split
+    (2048, 256, 64, 8, 384, "bf16", "bf16", None),     # prefill, near-uniform routing: most experts
+    (2048, 256, 64, 8, 384, "bf16", "fp8_e4m3fn", None),  # 200-300 rows, split into balanced tiles
     (33, 200, 7, 3, 72, "f32", "f32", None),           # fp32 streaming
 ])
 def test_ffn_paths_and_splits(dev, T, d, E, k, d_ff, act, w, zipf):

@@ -17,15 +17,16 @@
 // one of them from its row count, decided on the device):
 //  - ffn_stream_kernel: weights straight from HBM into MFMA operand registers, 16-row items,
 //    the contraction split over the 4 waves and reduced through LDS in a fixed order; fp32,
-//    widths not multiples of 64, and experts with <= 16 rows in decode-sized fp8 launches.
+//    widths not multiples of 64, and, beside the register-staged tiles, experts with <= 16
+//    rows in fp8 launches longer than the direct-to-LDS kernel takes.
 //  - dl_tiles (in ffn_tiled_dl_kernel and ffn_prefill_kernel): tiles loaded straight into a
 //    ring of LDS slots by buffer loads, XOR-swizzled for conflict-free fragment reads, on a
-//    persistent grid whose rounds of tiles are dealt to the XCDs in runs; decode-sized bf16
-//    launches (64 x 128 tiles, with a contraction split when there are few tiles) and, in
+//    persistent grid whose rounds of tiles are dealt to the XCDs in runs; decode-sized
+//    launches (64 x 128 tiles; bf16 with a contraction split when there are few tiles) and, in
 //    ffn_prefill_kernel, both roles of prefill-sized launches: workgroups streaming the experts
 //    with <= 16 rows beside workgroups running 256-row tiles of the others.
-//  - ffn_tiled_kernel: the older register-staged tiles, for fp8 weights in decode-sized
-//    launches.
+//  - ffn_tiled_kernel: the older register-staged tiles, kept for fp8 weights whose contraction
+//    (d or d_ff) is longer than 65536, beyond what the direct-to-LDS kernel stages scales for.
 //
 // fp8 weights (OCP e4m3fn, fp32 scale per 128x128 block): codes are converted exactly to bf16
 // in registers, each 128-long contraction block is accumulated from zero in fp32 and then
@@ -461,7 +462,8 @@ static hipError_t launch_stream(const StreamArgs& p, const DeviceInfo& dev, hipS
 // gate/up pass, gate and up columns c0 + wn*WN/2.. (so SwiGLU is applied in registers).
 // Two shapes are instantiated: 64 x 64 per wave for decode-sized batches and 128 x 128 per
 // wave (256 fp32 accumulators per lane, in AGPRs) for prefill, where a larger tile halves
-// the LDS and L2 traffic per MFMA.
+// the LDS and L2 traffic per MFMA. (Only fp8 weights with a contraction longer than 65536
+// reach this kernel now; the direct-to-LDS tiles below take every other tiled launch.)
 // LDS tiles hold 64-wide rows of bf16 (128 bytes = 8 chunks of 16 bytes) with an XOR
 // swizzle: chunk c of row r is stored at chunk c ^ ((r >> 1) & 7). A 16-byte fragment load
 // reads one chunk from each of 16 consecutive rows, and the staging store writes the 8 chunks
@@ -1481,14 +1483,19 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.rows == 0) return hipSuccess;
   // Which kernel takes which expert (decided per expert on the device from its row count):
   //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
-  //  - decode-sized batches (T*k < 32*E): bf16 weights go to the 64 x 128 direct-to-LDS tiles
-  //    for every expert; fp8 weights stream experts with <= 16 rows and tile the rest;
+  //  - decode-sized batches (T*k < 32*E): the 64 x 128 direct-to-LDS tiles take every expert
+  //    (bf16 and fp8 weights);
   //  - prefill-sized batches: one launch per GEMM whose workgroups split into a streaming role
   //    (experts with <= 16 rows, 16 x 256 tiles) and a large-tile role (the rest).
   const bool tiled = a.act == MOE_BF16 && a.d % kTK == 0 && a.d_ff % kTK == 0;
   const bool big = (long long)a.rows >= 32LL * a.E;
   int small = tiled ? kStreamMaxRows : 0x7fffffff;
-  if (tiled && !big && a.wdt == MOE_BF16) small = 0;
+  // fp8 at decode sizes: every expert on the direct-to-LDS tiles, except in launches so small
+  // that bf16 would split the contraction (at most a few rows in all), where streaming the
+  // small experts, whose kernel splits each item's contraction over its waves, is faster
+  const bool fp8_dl_small = a.wdt == MOE_FP8_E4M3FN && tiled && !big && a.d <= kFp8DlMaxK &&
+                            a.d_ff <= kFp8DlMaxK && !split_gemm(a.rows, a.E, a.d_ff, 64);
+  if (tiled && !big && (a.wdt == MOE_BF16 || fp8_dl_small)) small = 0;
   StreamArgs gu{a.x_sorted, a.w_gate, a.w_up, a.s_gate, a.s_up, a.h, a.offsets,
                 a.E, a.d, a.d_ff, a.rows, small};
   StreamArgs dn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
@@ -1540,16 +1547,22 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
                                              : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
-  // fp8 weights outside the prefill kernel's range: small experts stream, the rest go to the
-  // register-staged tiles
-  st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
+  // fp8 weights outside the prefill kernel: decode-sized launches run their tiled experts on
+  // the direct-to-LDS tiles (64 x 128, 64-wide steps in a 4-slot ring; every expert, as for
+  // bf16, unless the launch is tiny); prefill-sized launches, or contractions longer than the
+  // direct-to-LDS kernel stages scales for, stream the experts with <= 16 rows and run the rest
+  // on the register-staged tiles
+  const bool fp8_dl_dec = !big && a.d <= kFp8DlMaxK && a.d_ff <= kFp8DlMaxK;
+  if (!fp8_dl_small) st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = big ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
-             : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
-  if (st == hipSuccess) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
+    st = fp8_dl_dec ? launch_tiled_dl<kFP8, true, 32, 64, 2, 2, 4, 64>(tgu, dev, stream)
+         : big        ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
+                      : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
+  if (st == hipSuccess && !fp8_dl_small) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = big ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
-             : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
+    st = fp8_dl_dec ? launch_tiled_dl<kFP8, false, 32, 64, 2, 2, 4, 64>(tdn, dev, stream)
+         : big        ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
+                      : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
   return st;
 }
 

@@ -1552,15 +1552,22 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   // bf16, unless the launch is tiny); prefill-sized launches, or contractions longer than the
   // direct-to-LDS kernel stages scales for, stream the experts with <= 16 rows and run the rest
   // on the register-staged tiles
+  // With at most 8 rows per expert on average the tiles are 32 rows tall with 128-wide steps in
+  // a 3-slot ring (24 KB slots, two workgroups per CU: 16 KB of weights per step, as the bf16
+  // tiles load); more rows per expert take 64-row tiles with 64-wide steps in a 4-slot ring,
+  // which re-read an expert's weights for half as many row tiles.
   const bool fp8_dl_dec = !big && a.d <= kFp8DlMaxK && a.d_ff <= kFp8DlMaxK;
+  const bool fp8_short = (long long)a.rows <= 8LL * a.E;
   if (!fp8_dl_small) st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl_dec ? launch_tiled_dl<kFP8, true, 32, 64, 2, 2, 4, 64>(tgu, dev, stream)
+    st = fp8_dl_dec ? (fp8_short ? launch_tiled_dl<kFP8, true, 16, 64, 2, 2, 3, 128>(tgu, dev, stream)
+                                 : launch_tiled_dl<kFP8, true, 32, 64, 2, 2, 4, 64>(tgu, dev, stream))
          : big        ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
                       : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
   if (st == hipSuccess && !fp8_dl_small) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl_dec ? launch_tiled_dl<kFP8, false, 32, 64, 2, 2, 4, 64>(tdn, dev, stream)
+    st = fp8_dl_dec ? (fp8_short ? launch_tiled_dl<kFP8, false, 16, 64, 2, 2, 3, 128>(tdn, dev, stream)
+                                 : launch_tiled_dl<kFP8, false, 32, 64, 2, 2, 4, 64>(tdn, dev, stream))
          : big        ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
                       : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
   return st;

@@ -330,7 +330,7 @@ def check_capacity_vs_library():
 def check_capacity_brute_force_layer():
     for seed, (T, d, E, k, d_ff) in enumerate([(20, 6, 4, 2, 8), (33, 5, 6, 3, 7), (16, 8, 3, 1, 4)]):
         logits, x, W = tiny_case(T, d, E, k, d_ff, 300 + seed)
-        for cap in (0, 1, 3, 7, T):
+        for cap in (1, 3, 7, T, 0):
             ref, _, _ = brute_force_layer(logits, x, W, k, cap)
             out = run_oracle(logits, x, W, k, cap)
             if cap == 0:
@@ -401,7 +401,8 @@ def test_oracle_pin(check):
 # the pins must catch plausible mistakes planted in the oracle
 # ----------------------------------------------------------------------------------------
 _ORIG = {n: getattr(om, n) for n in ("route", "permute", "combine", "decode_e4m3fn", "expert_ffn", "decode_bf16",
-                                     "expert_capacity", "router_logits", "rel_max_err", "expert_down")}
+                                     "expert_capacity", "router_logits", "rel_max_err", "expert_down", "ffn",
+                                     "make_weight_decoder")}
 
 
 def _mut_route_tie_high(logits, k):
@@ -490,25 +491,54 @@ def _mut_combine_keeps_dropped(y_sorted, flat_to_sorted, gates):
     return y
 
 
-def _mut_ffn_silu_on_up(X, Wg, Wu, Wd, return_h=False):
+def _mut_h_round(h, h_round):
+    return om.round_bf16_value(h) if h_round == "bf16" else h
+
+
+def _mut_ffn_silu_on_up(X, Wg, Wu, Wd, return_h=False, h_round=None):
     G, U = X @ Wg.T, X @ Wu.T
-    h = om.silu(U) * G
+    h = _mut_h_round(om.silu(U) * G, h_round)
     y = h @ Wd.T
     return (y, h) if return_h else y
 
 
-def _mut_ffn_sigmoid_only(X, Wg, Wu, Wd, return_h=False):
+def _mut_ffn_sigmoid_only(X, Wg, Wu, Wd, return_h=False, h_round=None):
     G, U = X @ Wg.T, X @ Wu.T
-    h = (1.0 / (1.0 + np.exp(-G))) * U
+    h = _mut_h_round((1.0 / (1.0 + np.exp(-G))) * U, h_round)
     y = h @ Wd.T
     return (y, h) if return_h else y
 
 
-def _mut_ffn_down_untransposed(X, Wg, Wu, Wd, return_h=False):
+def _mut_ffn_down_untransposed(X, Wg, Wu, Wd, return_h=False, h_round=None):
     G, U = X @ Wg.T, X @ Wu.T
-    h = om.silu(G) * U
+    h = _mut_h_round(om.silu(G) * U, h_round)
     y = h @ Wd if Wd.shape[0] == Wd.shape[1] else h @ Wd.T[:, ::-1]
     return (y, h) if return_h else y
+
+
+def _mut_grouped_ffn_expert_shift(x_sorted, offsets, expert_weights, return_h=False, h_round=None):
+    # each segment goes through the next expert's weights (segment index off by one)
+    E = len(offsets) - 1
+    return _ORIG["ffn"](x_sorted, offsets, lambda e: expert_weights((e + 1) % E), return_h, h_round)
+
+
+def _mut_grouped_ffn_last_row_skipped(x_sorted, offsets, expert_weights, return_h=False, h_round=None):
+    # every non-empty segment stops one row short (end taken as inclusive-minus-one)
+    off = np.asarray(offsets).copy()
+    out = _ORIG["ffn"](x_sorted, off, expert_weights, return_h, h_round)
+    y = out[0] if return_h else out
+    for e in range(len(off) - 1):
+        if off[e + 1] > off[e]:
+            y[off[e + 1] - 1] = 0.0
+    return out
+
+
+def _mut_decoder_gate_up_swapped(raw_weights, w_fmt):
+    dec = _ORIG["make_weight_decoder"](raw_weights, w_fmt)
+    def swapped(e):
+        g, u, d = dec(e)
+        return u, g, d
+    return swapped
 
 
 def _mut_combine_unweighted(y_sorted, flat_to_sorted, gates):
@@ -589,6 +619,9 @@ MUTANTS = {
     "ffn_silu_on_up": ("expert_ffn", _mut_ffn_silu_on_up),
     "ffn_sigmoid_only": ("expert_ffn", _mut_ffn_sigmoid_only),
     "ffn_down_untransposed": ("expert_ffn", _mut_ffn_down_untransposed),
+    "grouped_ffn_expert_shift": ("ffn", _mut_grouped_ffn_expert_shift),
+    "grouped_ffn_last_row_skipped": ("ffn", _mut_grouped_ffn_last_row_skipped),
+    "decoder_gate_up_swapped": ("make_weight_decoder", _mut_decoder_gate_up_swapped),
     "combine_unweighted": ("combine", _mut_combine_unweighted),
     "combine_wrong_map": ("combine", _mut_combine_wrong_map),
     "decode_bf16_shift": ("decode_bf16", _mut_decode_bf16_shift),
@@ -611,6 +644,8 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     for check in CHECKS:
         try:
             check()
+        except TypeError:
+            raise  # a mutant whose signature does not fit its callers never ran: no catch
         except Exception:  # an assertion or a shape error both count as caught
             failures += 1
     assert failures > 0, f"no pin caught mutant {name}"

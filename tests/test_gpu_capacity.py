@@ -98,19 +98,28 @@ def test_permute_capacity_prefill_size(dev):
         assert np.array_equal(out["sorted_to_flat"][:kept].cpu().numpy(), ref["sorted_to_flat"])
 
 
-@pytest.mark.parametrize("T,E,k,cap_pct", [
-    (9000, 1, 1, None),     # one expert
-    (1000, 17, 9, None),    # the last 16-expert scan workgroup holds one expert
-    (600, 1024, 16, None),  # the expert limit: every rank wavefront scans 16 counts per lane
-    (40000, 33, 8, None),   # 1,250 tiles: more than the scan keeps in registers
-    (3000, 300, 4, 110),    # capacity on a partial scan workgroup
+@pytest.mark.parametrize("T,E,k,cap_pct,zipf", [
+    (9000, 1, 1, None, 0),       # one expert
+    (1000, 17, 9, None, 0),      # the last 16-expert scan workgroup holds one expert
+    (600, 1024, 16, None, 0),    # the expert limit: every rank wavefront scans 16 counts per lane
+    (40000, 33, 8, None, 0),     # 1,250 tiles: more than the scan keeps in registers
+    (3000, 300, 4, 110, 0),      # capacity on a partial scan workgroup
+    (8193, 256, 1, None, 0),     # one assignment past the one-workgroup kernel: count-and-rank launch
+    (2731, 200, 3, None, 1.5),   # the same with 200 experts, skewed (a hot expert per wave)
+    (16384, 256, 4, 125, 1.5),   # count-and-rank at its largest batch, capacity, skewed
+    (8200, 256, 8, 125, 0),      # 65,600 assignments: histogram and rank launches, capacity
+    (12000, 257, 2, None, 1.2),  # 257 experts: histogram and rank launches
 ])
-def test_permute_large_batches(dev, T, E, k, cap_pct):
+def test_permute_large_batches(dev, T, E, k, cap_pct, zipf):
     """The multi-launch permutation (more than 8192 assignments) at expert counts and tile
-    counts the prefill workloads do not reach: counts, offsets, both maps and the sorted rows
-    bit for bit against the oracle's stable counting sort."""
+    counts the prefill workloads do not reach, and on both sides of the count-and-rank
+    kernel's limits: counts, offsets, both maps and the sorted rows bit for bit against the
+    oracle's stable counting sort."""
     rng = np.random.default_rng(T * 31 + E)
-    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)  # k distinct experts
+    # k distinct experts per token: top k of Gumbel-perturbed log weights (Zipf weights when
+    # zipf > 0, uniform otherwise)
+    logw = -zipf * np.log(np.arange(1, E + 1, dtype=np.float64))
+    ids = np.argsort(-(logw + rng.gumbel(size=(T, E))), axis=1)[:, :k].astype(np.int32)
     x = rng.integers(-32768, 32768, size=(T, 8), dtype=np.int16)          # bf16 bit patterns
     cap = None if cap_pct is None else moe.moe_expert_capacity(T, E, k, cap_pct)
     ref = oracle.permute(ids, E, cap)

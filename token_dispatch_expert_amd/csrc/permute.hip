@@ -12,8 +12,8 @@
 // Every position is still ranked among all of the expert's assignments, and a position at or
 // past the expert's capped end is dropped, so capping costs nothing extra.
 //
-// Batches of more than kSmallR assignments take three launches, none using float atomics, all
-// deterministic (smaller batches use one workgroup for the index work, see
+// Batches of more than kSmallR assignments take two or three launches, none using float
+// atomics, all deterministic (smaller batches use one workgroup for the index work, see
 // permute_small_kernel):
 //   hist : one workgroup per tile of kPermuteTile flat entries; LDS histogram -> ws[tile][e]
 //   rank : one 1024-thread workgroup per tile. It sums, per expert, the histograms of the tiles
@@ -27,6 +27,8 @@
 //          index maps.
 //   copy : one workgroup per token reads x[t] once in 16-byte vectors and stores it to its
 //          k sorted rows.
+// Mid-size batches (at most kCountMaxR assignments, at most kCountMaxE experts) replace hist
+// and rank by one launch whose workgroups count the ids themselves (permute_count_rank_kernel).
 // (A separate scan launch between hist and rank, with the expert offsets scanned again by
 // every rank wavefront, took one more dependent launch: ~6 us of the 8192-token index phase.)
 #include <mutex>
@@ -95,54 +97,21 @@ __device__ __forceinline__ int block_inclusive_scan_1024(int v, int32_t* wave_su
 constexpr int kRankThreads = 1024;  // = kScanThreads: the block scan below is the 1024-thread one
 static_assert(kRankThreads >= MOE_MAX_EXPERTS, "one thread per expert in the offsets scan");
 
-// One workgroup per tile t. Thread (q, e) sums expert e's histogram entries over slice q of the
-// tiles (all of them, and those before t), loads issued 16 at a time; the slices are added in
-// LDS in a fixed order.
-__global__ __launch_bounds__(kRankThreads) void permute_rank_kernel(const int32_t* __restrict__ ids,
-                                                                    int R, int E, int nbits, int cap,
-                                                                    const int32_t* __restrict__ hist,
-                                                                    int n_tiles,
-                                                                    int32_t* __restrict__ counts,
-                                                                    int32_t* __restrict__ offsets,
-                                                                    int32_t* __restrict__ s2f,
-                                                                    int32_t* __restrict__ f2s) {
-  __shared__ int32_t pre_s[kRankThreads], tot_s[kRankThreads];
+// The rank step of tile t, once thread e < E holds `base` (expert e's assignments in the tiles
+// before t) and `tot` (all of expert e's assignments); other threads hold zeros. A block scan
+// of the kept counts gives the expert offsets (tile 0's workgroup stores counts and offsets).
+// The first wavefront then walks the tile's entries in flat order, 64 at a time: lanes with the
+// same expert find each other with ballots over the expert id's bits, so a lane's rank among
+// equal keys is a popcount of lower lanes, and the group's last lane advances the running
+// position in LDS. Writes both index maps.
+__device__ __forceinline__ void rank_tile(const int32_t* __restrict__ ids, int R, int E, int nbits,
+                                          int cap, int t, int base, int tot,
+                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                          int32_t* __restrict__ s2f, int32_t* __restrict__ f2s) {
   __shared__ int32_t run[MOE_MAX_EXPERTS], lim[MOE_MAX_EXPERTS];
   __shared__ int32_t wave_sum[kRankThreads / kWave];
   const int tid = threadIdx.x;
-  const int t = blockIdx.x;
-  int Ep = 1;
-  while (Ep < E) Ep <<= 1;  // <= 1024
-  const int Q = kRankThreads / Ep;
-  const int e = tid % Ep, q = tid / Ep;
-  const int tpq = (n_tiles + Q - 1) / Q;
-  const int t0 = min(q * tpq, n_tiles), t1 = min(t0 + tpq, n_tiles);
-  int pre = 0, tot = 0;
-  if (e < E) {
-    constexpr int B = 16;
-    for (int tb = t0; tb < t1; tb += B) {
-      int h[B];
-#pragma unroll
-      for (int u = 0; u < B; ++u) h[u] = tb + u < t1 ? hist[(size_t)(tb + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < B; ++u) {
-        tot += h[u];
-        pre += tb + u < t ? h[u] : 0;
-      }
-    }
-  }
-  pre_s[tid] = pre;
-  tot_s[tid] = tot;
-  __syncthreads();
-  int kept = 0, base = 0;
-  if (tid < E) {
-    int tt = 0;
-    for (int qq = 0; qq < Q; ++qq) {
-      tt += tot_s[qq * Ep + tid];
-      base += pre_s[qq * Ep + tid];
-    }
-    kept = min(tt, cap);  // kept assignments (capacity factor)
-  }
+  const int kept = tid < E ? min(tot, cap) : 0;  // kept assignments (capacity factor)
   const int incl = block_inclusive_scan_1024(kept, wave_sum);
   if (tid < E) {
     const int o = incl - kept;  // the expert's first row
@@ -194,6 +163,105 @@ __global__ __launch_bounds__(kRankThreads) void permute_rank_kernel(const int32_
     if (valid && (63 - __clzll(same)) == lane) run[ek] += __popcll(same);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// One workgroup per tile t. Thread (q, e) sums expert e's histogram entries over slice q of the
+// tiles (all of them, and those before t), loads issued 16 at a time; the slices are added in
+// LDS in a fixed order; then rank_tile.
+__global__ __launch_bounds__(kRankThreads) void permute_rank_kernel(const int32_t* __restrict__ ids,
+                                                                    int R, int E, int nbits, int cap,
+                                                                    const int32_t* __restrict__ hist,
+                                                                    int n_tiles,
+                                                                    int32_t* __restrict__ counts,
+                                                                    int32_t* __restrict__ offsets,
+                                                                    int32_t* __restrict__ s2f,
+                                                                    int32_t* __restrict__ f2s) {
+  __shared__ int32_t pre_s[kRankThreads], tot_s[kRankThreads];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;  // <= 1024
+  const int Q = kRankThreads / Ep;
+  const int e = tid % Ep, q = tid / Ep;
+  const int tpq = (n_tiles + Q - 1) / Q;
+  const int t0 = min(q * tpq, n_tiles), t1 = min(t0 + tpq, n_tiles);
+  int pre = 0, tot = 0;
+  if (e < E) {
+    constexpr int B = 16;
+    for (int tb = t0; tb < t1; tb += B) {
+      int h[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) h[u] = tb + u < t1 ? hist[(size_t)(tb + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        tot += h[u];
+        pre += tb + u < t ? h[u] : 0;
+      }
+    }
+  }
+  pre_s[tid] = pre;
+  tot_s[tid] = tot;
+  __syncthreads();
+  int base = 0, tt = 0;
+  if (tid < E) {
+    for (int qq = 0; qq < Q; ++qq) {
+      tt += tot_s[qq * Ep + tid];
+      base += pre_s[qq * Ep + tid];
+    }
+  }
+  rank_tile(ids, R, E, nbits, cap, t, base, tt, counts, offsets, s2f, f2s);
+}
+
+// Mid-size batches (R <= kCountMaxR, E <= kCountMaxE): one launch does the counting and the
+// ranking. Every tile's workgroup counts the whole batch itself (the ids are R * 4 bytes, as
+// many as the tile histograms the rank kernel above reads when E = kPermuteTile) into per-wave
+// LDS histograms, split at its own tile's start, which saves the histogram launch; then
+// rank_tile. Wave w counts the 64-entry chunks w, w + 16, w + 32, ..., kCountBatch loads in
+// flight; its histograms are its own, so only lanes of one instruction share an address (LDS
+// atomic adds). (64 loads in flight instead of 32 measured the same at 65,536 assignments.)
+constexpr int kCountMaxR = 65536;
+constexpr int kCountMaxE = 256;
+constexpr int kCountBatch = 32;
+__global__ __launch_bounds__(kRankThreads) void permute_count_rank_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int nbits, int cap, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ s2f, int32_t* __restrict__ f2s) {
+  constexpr int NWV = kRankThreads / kWave;
+  __shared__ int32_t before[NWV * kCountMaxE], from[NWV * kCountMaxE];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int t = blockIdx.x;
+  const int base_i = t * kPermuteTile;  // a multiple of 64: no chunk straddles it
+  for (int i = tid; i < NWV * kCountMaxE; i += kRankThreads) {
+    before[i] = 0;
+    from[i] = 0;
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t all_ids =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, R * 4, kRawBufferWord3);
+  const int nchunks = (R + kWave - 1) / kWave;
+  int32_t* mine_before = before + wave * kCountMaxE;
+  int32_t* mine_from = from + wave * kCountMaxE;
+  for (int c0 = wave; c0 < nchunks; c0 += NWV * kCountBatch) {
+    int key[kCountBatch];
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) key[u] = load_tile_id(all_ids, (c0 + u * NWV) * kWave + lane);
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int c = c0 + u * NWV;
+      if (c * kWave + lane < R)
+        atomicAdd((c * kWave < base_i ? mine_before : mine_from) + clamp_expert(key[u], E), 1);
+    }
+  }
+  __syncthreads();
+  int base = 0, tot = 0;
+  if (tid < E) {
+    for (int w = 0; w < NWV; ++w) {
+      base += before[w * kCountMaxE + tid];
+      tot += from[w * kCountMaxE + tid];
+    }
+    tot += base;
+  }
+  rank_tile(ids, R, E, nbits, cap, t, base, tot, counts, offsets, s2f, f2s);
 }
 
 __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restrict__ x, int k,
@@ -361,11 +429,17 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* ids, int
     hipError_t st = launch_fill_i32(counts, E, 0, stream);
     return st == hipSuccess ? launch_fill_i32(offsets, E + 1, 0, stream) : st;
   }
-  permute_hist_kernel<<<n_tiles, 256, lds, stream>>>(ids, R, E, ws);
-  hipError_t st = hipGetLastError();
-  if (st != hipSuccess) return st;
-  permute_rank_kernel<<<n_tiles, kRankThreads, 0, stream>>>(ids, R, E, nbits, cap, ws, n_tiles, counts,
-                                                             offsets, sorted_to_flat, flat_to_sorted);
+  hipError_t st;
+  if (R <= kCountMaxR && E <= kCountMaxE) {
+    permute_count_rank_kernel<<<n_tiles, kRankThreads, 0, stream>>>(ids, R, E, nbits, cap, counts, offsets,
+                                                                     sorted_to_flat, flat_to_sorted);
+  } else {
+    permute_hist_kernel<<<n_tiles, 256, lds, stream>>>(ids, R, E, ws);
+    st = hipGetLastError();
+    if (st != hipSuccess) return st;
+    permute_rank_kernel<<<n_tiles, kRankThreads, 0, stream>>>(ids, R, E, nbits, cap, ws, n_tiles, counts,
+                                                               offsets, sorted_to_flat, flat_to_sorted);
+  }
   st = hipGetLastError();
   if (st != hipSuccess) return st;
   permute_copy_kernel<<<T, threads, 0, stream>>>(static_cast<const uint4*>(x), k, vpr,

@@ -179,8 +179,9 @@ moe_status_t moe_permute_capped(const void* x, moe_dtype_t x_dtype, const int32_
  * between the two GEMMs, and, for launches small enough that the contraction is split across
  * workgroups (rows < 32 * E, bf16 activations and weights, and at most 256 tiles of 64 rows by
  * 64 h columns, or by 128 output columns, counting every expert that could hold a row), 16 MiB
- * of fp32 partial tiles after h; for prefill-sized launches (rows >= 32 * E, bf16 activations,
- * bf16 weights, or fp8 weights with d and d_ff at most 65536) a 256-byte header and 64 MiB
+ * of fp32 partial tiles after h; for prefill-sized launches (bf16 activations; bf16 weights
+ * with rows >= 32 * E, or fp8 weights with rows > 8 * E and d and d_ff at most 65536) a
+ * 256-byte header and 64 MiB
  * (bf16) or 32 MiB (fp8) of fp32 partial tiles for the last round's tiles, whose contraction is
  * split across workgroups. */
 size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_dtype,

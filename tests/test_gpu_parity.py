@@ -214,16 +214,18 @@ def test_prefill_tile_paths(dev, w, E, zipf):
     assert cfg.T * cfg.k >= 32 * cfg.E
 
 
-def test_fp8_small(dev):
-    run_full(synth.tiny_config(T=90, d=256, E=6, k=2, d_ff=384, act="bf16", w="fp8_e4m3fn",
+@pytest.mark.parametrize("T", [24, 90])
+def test_fp8_small(dev, T):
+    # T = 24: 8 rows per expert, the decode-sized fp8 tiles; T = 90: the prefill kernel
+    run_full(synth.tiny_config(T=T, d=256, E=6, k=2, d_ff=384, act="bf16", w="fp8_e4m3fn",
                                zipf_s=1.0, seed=8), dev)
 
 
 @pytest.mark.parametrize("T", [20, 80])
 def test_fp8_long_contraction(dev, T):
     # fp8 weights with d > 65536: the direct-to-LDS kernels stage an item's scale rows in LDS up
-    # to that length, so these launches take the register-staged tiles (decode-sized at T = 20,
-    # prefill-sized at T = 80) beside the streaming kernel for experts with <= 16 rows
+    # to that length, so these launches take the register-staged tiles (64-row tiles at T = 20,
+    # 128-row at T = 80) beside the streaming kernel for experts with <= 16 rows
     cfg = synth.tiny_config(T=T, d=65664, E=2, k=1, d_ff=128, act="bf16", w="fp8_e4m3fn",
                             zipf_s=1.5, seed=9)
     assert (cfg.T * cfg.k >= 32 * cfg.E) == (T == 80)
@@ -404,7 +406,9 @@ def test_decode_few_experts_long_contraction(dev, T, E, k):
     (2048, 256, 64, 8, 384, "bf16", "bf16", None),     # prefill, near-uniform routing: most experts
     (2048, 256, 64, 8, 384, "bf16", "fp8_e4m3fn", None),  # 200-300 rows, split into balanced tiles
     (33, 200, 7, 3, 72, "f32", "f32", None),           # fp32 streaming
-    (256, 512, 64, 4, 384, "bf16", "fp8_e4m3fn", 1.0),  # fp8 decode: direct-to-LDS tiles + streaming
+    (256, 512, 64, 4, 384, "bf16", "fp8_e4m3fn", 1.0),  # fp8, 16 rows per expert: the prefill kernel
+    (128, 512, 64, 4, 384, "bf16", "fp8_e4m3fn", 1.0),  # fp8 decode (8 rows per expert): direct-to-LDS tiles
+    (5, 1024, 16, 2, 512, "bf16", "fp8_e4m3fn", 1.0),   # tiny fp8 decode: streaming + direct-to-LDS tiles
 ])
 def test_ffn_paths_and_splits(dev, T, d, E, k, d_ff, act, w, zipf):
     # the kernel paths the sizes select, including both contraction splits, against the oracle,

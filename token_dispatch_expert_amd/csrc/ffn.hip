@@ -22,7 +22,8 @@
 //  - dl_tiles (in ffn_tiled_dl_kernel and ffn_prefill_kernel): tiles loaded straight into a
 //    ring of LDS slots by buffer loads, XOR-swizzled for conflict-free fragment reads, on a
 //    persistent grid whose rounds of tiles are dealt to the XCDs in runs; decode-sized
-//    launches (64 x 128 tiles; bf16 with a contraction split when there are few tiles) and, in
+//    launches (bf16: 64 x 128 tiles, with a contraction split when there are few tiles; fp8:
+//    32 x 128) and, in
 //    ffn_prefill_kernel, both roles of prefill-sized launches: workgroups streaming the experts
 //    with <= 16 rows beside workgroups running 256-row tiles of the others.
 //  - ffn_tiled_kernel: the older register-staged tiles, kept for fp8 weights whose contraction
@@ -1427,9 +1428,19 @@ static bool split_gemm(int rows, int E, int N, int cols_per_tile) {
   const long long tiles = nt * ((rows + 63) / 64 + (long long)(E < rows ? E : rows));
   return tiles <= kSplitMaxUnits / 2;
 }
+// Prefill-sized launches (the host knows the sizes, not the routing): bf16 weights from 32 rows
+// per configured expert; fp8 weights from more than 8. With fp8 weights the prefill kernel beat
+// the decode-sized tiles by 11-32% on every routing measured between 8 and 32 rows per expert
+// (Zipf 0 and 1.2, both model shapes) and tied at 8; with bf16 weights the better of the two
+// there depends on the routing's skew (near-uniform routings, every expert with ~30 rows, run
+// 5-38% faster on the decode-sized tiles, skewed ones 8-17% faster on the prefill kernel), so
+// the bf16 switch stays where the prefill kernel wins whatever the routing.
+static bool prefill_sized(int rows, int E, moe_dtype_t wdt) {
+  return wdt == MOE_FP8_E4M3FN ? (long long)rows > 8LL * E : (long long)rows >= 32LL * E;
+}
 static bool decode_tiled_bf16(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
   return act == MOE_BF16 && wdt == MOE_BF16 && d % kTK == 0 && d_ff % kTK == 0 &&
-         (long long)rows < 32LL * E;
+         !prefill_sized(rows, E, wdt);
 }
 static bool uses_split(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
   return decode_tiled_bf16(rows, E, d, d_ff, act, wdt) &&
@@ -1440,7 +1451,7 @@ constexpr size_t kPartialBytes = (size_t)kSplitMaxUnits * kSplitTileElems * size
 // Prefill-sized launches run ffn_prefill_kernel, whose last round's tiles may be split: a
 // 256-byte header and kTailMaxUnits partial tiles of the hot tile size follow h.
 static bool prefill_tiled(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
-  return act == MOE_BF16 && d % kTK == 0 && d_ff % kTK == 0 && (long long)rows >= 32LL * E &&
+  return act == MOE_BF16 && d % kTK == 0 && d_ff % kTK == 0 && prefill_sized(rows, E, wdt) &&
          (wdt == MOE_BF16 || (wdt == MOE_FP8_E4M3FN && d <= kFp8DlMaxK && d_ff <= kFp8DlMaxK));
 }
 constexpr size_t kHotTileElemsBF16 = 256 * 256, kHotTileElemsFP8 = 128 * 256;
@@ -1483,12 +1494,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
   if (a.rows == 0) return hipSuccess;
   // Which kernel takes which expert (decided per expert on the device from its row count):
   //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
-  //  - decode-sized batches (T*k < 32*E): the 64 x 128 direct-to-LDS tiles take every expert
-  //    (bf16 and fp8 weights);
+  //  - decode-sized batches (T*k < 32*E with bf16 weights, T*k <= 8*E with fp8 weights): the
+  //    direct-to-LDS tiles take every expert;
   //  - prefill-sized batches: one launch per GEMM whose workgroups split into a streaming role
   //    (experts with <= 16 rows, 16 x 256 tiles) and a large-tile role (the rest).
   const bool tiled = a.act == MOE_BF16 && a.d % kTK == 0 && a.d_ff % kTK == 0;
-  const bool big = (long long)a.rows >= 32LL * a.E;
+  const bool big = prefill_sized(a.rows, a.E, a.wdt);
   int small = tiled ? kStreamMaxRows : 0x7fffffff;
   // fp8 at decode sizes: every expert on the direct-to-LDS tiles, except in launches so small
   // that bf16 would split the contraction (at most a few rows in all), where streaming the
@@ -1547,28 +1558,23 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
                                              : launch_tiled_dl<kBF16, false, 32, 64, 2, 2, 3, 64>(tdn, dev, stream);
     return st;
   }
-  // fp8 weights outside the prefill kernel: decode-sized launches run their tiled experts on
-  // the direct-to-LDS tiles (64 x 128, 64-wide steps in a 4-slot ring; every expert, as for
-  // bf16, unless the launch is tiny); prefill-sized launches, or contractions longer than the
-  // direct-to-LDS kernel stages scales for, stream the experts with <= 16 rows and run the rest
-  // on the register-staged tiles
-  // With at most 8 rows per expert on average the tiles are 32 rows tall with 128-wide steps in
-  // a 3-slot ring (24 KB slots, two workgroups per CU: 16 KB of weights per step, as the bf16
-  // tiles load); more rows per expert take 64-row tiles with 64-wide steps in a 4-slot ring,
-  // which re-read an expert's weights for half as many row tiles.
+  // fp8 weights outside the prefill kernel: decode-sized launches (at most 8 rows per expert)
+  // run their tiled experts on the direct-to-LDS tiles, 32 rows tall with 128-wide steps in a
+  // 3-slot ring (24 KB slots, two workgroups per CU: 16 KB of weights per step, as the bf16
+  // tiles load), every expert as for bf16 unless the launch is tiny; contractions longer than
+  // the direct-to-LDS kernel stages scales for stream the experts with <= 16 rows and run the
+  // rest on the register-staged tiles (128 rows tall from 32 rows per expert, else 64)
   const bool fp8_dl_dec = !big && a.d <= kFp8DlMaxK && a.d_ff <= kFp8DlMaxK;
-  const bool fp8_short = (long long)a.rows <= 8LL * a.E;
+  const bool tall = (long long)a.rows >= 32LL * a.E;
   if (!fp8_dl_small) st = launch_stream<kBF16, kFP8, 2, 2, 2, 4>(gu, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl_dec ? (fp8_short ? launch_tiled_dl<kFP8, true, 16, 64, 2, 2, 3, 128>(tgu, dev, stream)
-                                 : launch_tiled_dl<kFP8, true, 32, 64, 2, 2, 4, 64>(tgu, dev, stream))
-         : big        ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
+    st = fp8_dl_dec ? launch_tiled_dl<kFP8, true, 16, 64, 2, 2, 3, 128>(tgu, dev, stream)
+         : tall       ? launch_tiled<kFP8, true, 128, 64, 2, 2>(tgu, dev, stream)
                       : launch_tiled<kFP8, true, 64, 64, 2, 2>(tgu, dev, stream);
   if (st == hipSuccess && !fp8_dl_small) st = launch_stream<kBF16, kFP8, 1, 4, 2, 4>(dn, dev, stream);
   if (st == hipSuccess && tiled)
-    st = fp8_dl_dec ? (fp8_short ? launch_tiled_dl<kFP8, false, 16, 64, 2, 2, 3, 128>(tdn, dev, stream)
-                                 : launch_tiled_dl<kFP8, false, 32, 64, 2, 2, 4, 64>(tdn, dev, stream))
-         : big        ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
+    st = fp8_dl_dec ? launch_tiled_dl<kFP8, false, 16, 64, 2, 2, 3, 128>(tdn, dev, stream)
+         : tall       ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
                       : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
   return st;
 }

@@ -15,8 +15,15 @@
  *    library never allocates or frees device memory and keeps no per-call state). Buffers
  *    must not overlap unless stated.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call
- *    only enqueues work on that stream and returns; it never synchronises. Results are
- *    valid once the stream has reached that point.
+ *    only enqueues work and returns; it never synchronises. Results are valid once the
+ *    stream has reached that point. Prefill-sized calls of moe_grouped_ffn with bf16 weights
+ *    (and the moe_layer calls that make them) may run the experts with few rows on a second
+ *    stream, one that the library creates for each (device, caller stream) on first use and
+ *    keeps until the process ends: it waits on an event recorded on `stream` at the start of
+ *    the call, and `stream` waits on an event recorded on it at the end, so everything
+ *    enqueued on `stream` afterwards sees the call's results, and the call can be captured in
+ *    a graph. Calls on one caller stream must not be enqueued from several threads at once
+ *    (they share that stream's two events).
  *  - Errors: all arguments are checked on the host before anything is enqueued; on any
  *    error nothing is enqueued and a status other than MOE_OK is returned. A failed kernel
  *    launch returns MOE_ERR_HIP. Device-side faults surface at the caller's next

@@ -1,8 +1,9 @@
 """moe_layer captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
 
-The library enqueues only kernels on the caller's stream (no allocation, no memset, no
-synchronisation), so a whole layer can be captured once and replayed, which removes the host
-launch cost from decode steps. Each replay is checked bit for bit against the eager call on the
+The library enqueues only kernels (no allocation, no memset, no synchronisation): on the
+caller's stream, and for prefill-sized bf16 layers also on a second stream forked from it and
+joined back with events, which a capture records as a branch of the graph. So a whole layer can
+be captured once and replayed, which removes the host launch cost from decode steps. Each replay is checked bit for bit against the eager call on the
 same inputs, with the outputs poisoned and other eager work on the device between replays."""
 import numpy as np
 import pytest

@@ -214,6 +214,37 @@ def test_prefill_tile_paths(dev, w, E, zipf):
     assert cfg.T * cfg.k >= 32 * cfg.E
 
 
+def _small_beside_large(counts, d, d_ff):
+    """Per GEMM (gate/up, down): whether the experts with 1..16 rows of a prefill-sized bf16
+    launch go to the lean streaming kernel on the library's second stream. This restates the
+    library's rule, which compares their weight bytes at 3.5 GB/s per CU with the other
+    experts' 256-row-tile-padded flops at 4 TFLOP/s per CU (the CU count cancels)."""
+    out = []
+    for N, K, mats in ((d_ff, d, 2), (d, d_ff, 1)):
+        small = sum(mats * N * K * 2 for n in counts if 0 < n <= 16)
+        large = sum(2 * ((n + 255) // 256 * 256) * K * mats * N for n in counts if n > 16)
+        out.append(small > 0 and large > 0 and small / 3.5e9 <= large / 4e12)
+    return out
+
+
+@pytest.mark.parametrize("zipf,lean", [(2.0, True), (0.9, False)])
+def test_prefill_small_experts_beside_tiles(dev, zipf, lean):
+    # A prefill-sized bf16 layer whose experts with <= 16 rows go to the lean kernel on the
+    # second stream beside the large tiles (few of them beside much tile work), or stay in the
+    # prefill kernel's streaming role (more of them): both checked element-wise.
+    cfg = synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16",
+                            zipf_s=zipf, seed=17)
+    assert cfg.T * cfg.k >= 32 * cfg.E
+    lg, _ = synth.make_routing_inputs(cfg)
+    ids, _ = oracle.route(lg, cfg.k)
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    regime = _small_beside_large(counts, cfg.d, cfg.d_ff)
+    print(f"small experts {int(((counts > 0) & (counts <= 16)).sum())}, lean (gate/up, down) {regime}",
+          flush=True)
+    assert regime == [lean, lean]
+    run_full(cfg, dev)
+
+
 @pytest.mark.parametrize("T", [24, 90])
 def test_fp8_small(dev, T):
     # T = 24: 8 rows per expert, the decode-sized fp8 tiles; T = 90: the prefill kernel

@@ -6,6 +6,7 @@
 // The only library state is a per-device cache of the compute-unit count.
 #include <climits>
 #include <mutex>
+#include <vector>
 
 #include "moe_internal.h"
 
@@ -28,6 +29,38 @@ hipError_t device_info(DeviceInfo* out) {
   }
   *out = cache[dev];
   return hipSuccess;
+}
+
+bool side_stream_for(hipStream_t caller, SideStream* out) {
+  static std::mutex mu;
+  struct Entry { int dev; hipStream_t caller; SideStream side; };
+  static std::vector<Entry> table;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& en : table)
+    if (en.dev == dev && en.caller == caller) {
+      *out = en.side;
+      return true;
+    }
+  // Creating a stream and events is allowed while a graph is being captured once this thread's
+  // capture mode is relaxed (the documented way to make such calls during a capture); the
+  // previous mode is restored afterwards.
+  hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+  if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) return false;
+  SideStream side;
+  bool ok = hipStreamCreateWithFlags(&side.stream, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&side.fork, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&side.join, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    if (side.fork) (void)hipEventDestroy(side.fork);
+    if (side.stream) (void)hipStreamDestroy(side.stream);
+  }
+  (void)hipThreadExchangeStreamCaptureMode(&mode);
+  if (!ok) return false;
+  table.push_back(Entry{dev, caller, side});
+  *out = side;
+  return true;
 }
 
 }  // namespace moe

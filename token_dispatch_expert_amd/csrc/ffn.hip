@@ -37,6 +37,8 @@
 #include <type_traits>
 #include <utility>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -490,6 +492,9 @@ struct TiledArgs {
   // tail split of prefill launches: {S, first split item, end of the split items}, written by
   // the launch that computes the chunks and read by the one that adds them
   int32_t* split_info = nullptr;
+  // prefill: 1 when ffn_lean_kernel runs beside this launch on a second stream and may take the
+  // experts with at most kStreamMaxRows rows (both kernels decide from the counts alike)
+  int lean = 0;
 };
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN>
@@ -1323,45 +1328,70 @@ static size_t dl_lds_bytes(const TiledArgs& p) {
 // than too many.
 constexpr float kColdCuGBps = 30.0f;    // weight streaming per CU, GB/s (effective)
 constexpr float kHotCuTflops = 4.0f;    // tile MFMA rate per CU, TFLOP/s
+// Work of the two kinds of experts of a prefill launch, from the counts, summed by one wave
+// (every lane gets the totals; the same code in every kernel that decides from them, so the
+// decisions agree): weight bytes of the experts with 1..kStreamMaxRows rows, and tile-padded
+// MFMA flops (row tiles of HTM) of the larger ones.
+template <bool GATED, int WB, int HTM>
+__device__ __forceinline__ void small_large_work(const TiledArgs& p, int lane, float& small_bytes,
+                                                 float& large_flops) {
+  small_bytes = 0.f;
+  large_flops = 0.f;
+  for (int e = lane; e < p.E; e += kWave) {
+    int a, b;
+    expert_rows(p.offsets, e, p.rows, a, b);
+    const int n = b - a;
+    const float wbytes = (GATED ? 2.f : 1.f) * (float)p.N * (float)p.K * WB;
+    const float padded = (float)((n + HTM - 1) / HTM * HTM);
+    const float flops = 2.f * padded * (float)p.K * (float)(GATED ? 2 * p.N : p.N);
+    small_bytes += (n > 0 && n <= kStreamMaxRows) ? wbytes : 0.f;
+    large_flops += n > kStreamMaxRows ? flops : 0.f;
+  }
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    small_bytes += __shfl_xor(small_bytes, off);
+    large_flops += __shfl_xor(large_flops, off);
+  }
+}
+// The lean kernel (below) takes the small experts when streaming their weights at its rate
+// beside the tiles ends no later than the large tiles on all G CUs would; otherwise the
+// prefill kernel keeps them in its streaming role and the lean kernel does nothing. Its rate
+// beside the large tiles is low, one wave per CU sharing the CU's memory pipeline with them:
+// ~0.9 TB/s on 256 CUs (c4 routing: 5.3 GB of gate/up weights in 5.8 ms), so the c4 routing's
+// 90 small experts stay in the streaming role while routings with fewer small experts beside
+// large ones (Zipf s = 0.6, 1.5, 2.5 at the c4 shape) move to the lean kernel.
+constexpr float kLeanCuGBps = 3.5f;  // the lean kernel's streaming rate per CU beside the tiles, GB/s
+__device__ __forceinline__ bool lean_takes_small(float small_bytes, float large_flops, int G) {
+  return small_bytes > 0.f && large_flops > 0.f &&
+         small_bytes / ((float)G * kLeanCuGBps * 1e9f) <= large_flops / ((float)G * kHotCuTflops * 1e12f);
+}
+
 template <int WF, bool GATED, int HWM, int HWN, int HRING, int HDK, int CWN, int CRING, int CDK>
 __global__ __launch_bounds__(512) void ffn_prefill_kernel(TiledArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int HTM = 2 * HWM, HTN = 4 * HWN;   // hot tiles: 2 x 4 waves
   constexpr int WB = WF == kFP8 ? 1 : 2;
   // work of each kind from the counts (one wave; the others wait at the barrier)
-  __shared__ float work[2];
+  __shared__ float work[3];
   if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    float cold_bytes = 0.f, hot_flops = 0.f;
-    for (int e = lane; e < p.E; e += kWave) {
-      int a, b;
-      expert_rows(p.offsets, e, p.rows, a, b);
-      const int n = b - a;
-      const float wbytes = (GATED ? 2.f : 1.f) * (float)p.N * (float)p.K * WB;
-      if (n > 0 && n <= kStreamMaxRows) cold_bytes += wbytes;
-      else if (n > kStreamMaxRows) {
-        const float padded = (float)((n + HTM - 1) / HTM * HTM);
-        hot_flops += 2.f * padded * (float)p.K * (float)(GATED ? 2 * p.N : p.N);
-      }
-    }
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-      cold_bytes += __shfl_xor(cold_bytes, off);
-      hot_flops += __shfl_xor(hot_flops, off);
-    }
-    if (lane == 0) {
+    float cold_bytes, hot_flops;
+    small_large_work<GATED, WB, HTM>(p, threadIdx.x, cold_bytes, hot_flops);
+    if (threadIdx.x == 0) {
       work[0] = cold_bytes / (kColdCuGBps * 1e9f);
       work[1] = hot_flops / (kHotCuTflops * 1e12f);
+      work[2] = (p.lean && lean_takes_small(cold_bytes, hot_flops, gridDim.x)) ? 1.f : 0.f;
     }
   }
   __syncthreads();
   const int G = gridDim.x;
   const float tc = work[0], th = work[1];
   // X is a multiple of 8 so that both roles keep the rank -> XCD pairing their tile order
-  // relies on (block b runs on XCD b % 8)
+  // relies on (block b runs on XCD b % 8); with the lean kernel taking the small experts every
+  // workgroup runs large tiles
   int X = 0;
   if (tc > 0.f) X = th > 0.f ? (int)(G * tc / (tc + th) / 8.f + 0.5f) * 8 : G;
   if (tc > 0.f && X < 8) X = 8 < G ? 8 : G;
   if (th > 0.f && X > G - 8) X = G - 8;
+  if (work[2] != 0.f) X = 0;
   X = __builtin_amdgcn_readfirstlane(X);
   __syncthreads();  // `work` is read by every thread before smem is reused
   // no hot role: an empty tail-split header for the launch that adds the chunks
@@ -1376,6 +1406,161 @@ __global__ __launch_bounds__(512) void ffn_prefill_kernel(TiledArgs p) {
   else
     dl_tiles<WF, GATED, HWM, HWN, 2, 4, HRING, HDK, false, 3, true>(p, smem, blockIdx.x - X, G - X,
                                                                     kStreamMaxRows, 0x7fffffff);
+}
+
+// Lean streaming kernel for the experts with 1..kStreamMaxRows rows of a prefill-sized bf16
+// launch, run on a second stream beside ffn_prefill_kernel so that every CU keeps its large
+// tiles: a large-tile workgroup leaves 32 VGPRs per SIMD and ~19.5 KB of LDS unused, and this
+// kernel's single-wave workgroups fit there (at most 32 VGPRs, kLeanRing * 6 KB of LDS). Each
+// wave streams its items through a private ring of direct-to-LDS loads (no barriers; the waits
+// are its own load counts) that runs on across item boundaries. An item is (expert, 16 gate and
+// the same 16 up columns of h) or (expert, 32 columns of y); a 64-wide step loads the item's
+// 16 activation rows (rows past the expert's last read as zeros) and its 32 weight rows,
+// 128 bytes each, into an XOR-swizzled slot, and runs 2 x 2 MFMAs. The weights are read once
+// and load with the non-temporal policy.
+// Whether workgroups of a and b bytes of LDS fit on one CU together (160 KB), with each
+// allocation rounded up to the allocation unit (512 bytes here; 1280 and 2048 are checked too,
+// so that a coarser unit could not leave the pair unable to share a CU).
+static inline bool lds_pair_fits(size_t a, size_t b) {
+  for (size_t unit : {size_t(512), size_t(1280), size_t(2048)})
+    if (align_up(a, unit) + align_up(b, unit) > size_t(160) * 1024) return false;
+  return true;
+}
+constexpr int kLeanRing = 3;         // (4 slots, with a 3-slot streaming role in the prefill kernel to
+                                     // make room, measured no faster)
+constexpr int kPrefillColdRing = 4;  // the prefill kernel's streaming-role ring (bf16)
+constexpr int kLeanSlotBytes = 6 * 1024;
+constexpr int kLeanLdsBytes = kLeanRing * kLeanSlotBytes;
+template <bool GATED, int HTM>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_num_vgpr(32))) void ffn_lean_kernel(TiledArgs p, int G,
+                                                                              const int32_t* __restrict__ offs) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x;
+  {
+    float sb, lf;
+    small_large_work<GATED, 2, HTM>(p, lane, sb, lf);
+    if (!p.lean || !lean_takes_small(sb, lf, G)) return;  // wave-uniform
+  }
+  constexpr int NC = GATED ? 16 : 32;  // output columns per item
+  const int NT = p.N / NC;             // N is a multiple of 64 on this path
+  const int nst = p.K / kDK;           // K is a multiple of 64
+  const size_t wstride = (size_t)p.N * p.K * 2;
+  // items in expert order (NT per small expert); this wave takes items blockIdx.x + j * gridDim.x
+  int total = 0;
+  for (int e = lane; e < p.E; e += kWave) {
+    int a, b;
+    expert_rows(p.offsets, e, p.rows, a, b);
+    total += (b - a > 0 && b - a <= kStreamMaxRows) ? NT : 0;
+  }
+  for (int off = kWave / 2; off >= 1; off >>= 1) total += __shfl_xor(total, off);
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int first = blockIdx.x, stride = gridDim.x;
+  const int mine = first < total ? (total - first + stride - 1) / stride : 0;
+  const int nsteps = mine * nst;  // < 2^31: at most E * N / 16 items of K / 64 steps
+  if (nsteps == 0) return;
+
+  // A walker over the small experts, moved forward item by item (items only increase): the
+  // expert holding item `it`, its rows and its first item
+  struct Walker { int e, base, r0, n; };
+  auto advance = [&](Walker& w, int it) __attribute__((always_inline)) {
+    while (w.e < p.E) {  // (the items counted above end before the last expert)
+      // a wave-uniform index, so these are scalar loads: a vector load here would make the
+      // compiler wait for every direct-to-LDS load in flight
+      const int e = __builtin_amdgcn_readfirstlane(w.e);
+      const int a = min(max(offs[e], 0), p.rows);
+      const int b = min(max(offs[e + 1], a), p.rows);
+      const int cnt = (b - a > 0 && b - a <= kStreamMaxRows) ? NT : 0;
+      if (it < w.base + cnt) { w.r0 = a; w.n = b - a; return; }
+      w.base += cnt;
+      ++w.e;
+    }
+    w.r0 = 0;
+    w.n = 0;
+  };
+  // lane offsets of the two load shapes (even and odd 8-row groups differ in their swizzle)
+  const int lr = lane >> 3;                              // row within an 8-row load
+  const int c0s = (lane & 7) ^ ((lr >> 1) & 7);          // source chunk, rows 0..7 of a group
+  const int c1s = (lane & 7) ^ (((8 + lr) >> 1) & 7);    // rows 8..15
+  const int off0 = lr * p.K * 2 + c0s * 16, off1 = lr * p.K * 2 + c1s * 16;
+  const int row8 = 8 * p.K * 2;                          // bytes of 8 operand rows
+
+  // issue side: the next step to load, as (item index j of this wave, step); compute side alike
+  Walker wi{0, 0, 0, 0}, wc{0, 0, 0, 0};
+  int ij = 0, ist = 0;
+  auto issue = [&](int g) __attribute__((always_inline)) {
+    const int it = first + ij * stride;
+    advance(wi, it);
+    const int c0 = (it - wi.base) * NC;
+    const uint8_t* Xt = static_cast<const uint8_t*>(p.X) + (size_t)wi.r0 * p.K * 2;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)Xt, (short)0, (int)((unsigned)wi.n * (unsigned)p.K * 2u), kBufferWord3);
+    const size_t wcol = (size_t)c0 * p.K * 2;
+    const unsigned bext = (unsigned)min((size_t)0xffffffffu, (size_t)(p.N - c0) * p.K * 2);
+    const __amdgpu_buffer_rsrc_t rB1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const uint8_t*>(p.W1) + (size_t)wi.e * wstride + wcol), (short)0, (int)bext, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rB2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const uint8_t*>(p.W2) + (size_t)wi.e * wstride + wcol), (short)0, (int)bext, kBufferWord3) : rB1;
+    u32x4* slot = reinterpret_cast<u32x4*>(smem + (g % kLeanRing) * kLeanSlotBytes);
+    const int ks = ist * kDK * 2;
+    // slot rows: 0..15 activations, 16..31 gate (or weight rows 0..15), 32..47 up (or 16..31)
+    buffer_load_lds16(rA, slot + 0 * 64, off0, ks);
+    buffer_load_lds16(rA, slot + 1 * 64, off1, row8 + ks);
+    buffer_load_lds16<kNonTemporal>(rB1, slot + 2 * 64, off0, ks);
+    buffer_load_lds16<kNonTemporal>(rB1, slot + 3 * 64, off1, row8 + ks);
+    buffer_load_lds16<kNonTemporal>(rB2, slot + 4 * 64, off0, (GATED ? 0 : 2 * row8) + ks);
+    buffer_load_lds16<kNonTemporal>(rB2, slot + 5 * 64, off1, (GATED ? 0 : 2 * row8) + row8 + ks);
+    if (++ist == nst) { ist = 0; ++ij; }
+  };
+  constexpr int kLoads = 6;  // load instructions per step
+
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int g = 0; g < kLeanRing && g < nsteps; ++g) issue(g);
+  int cj = 0, cst = 0;
+  for (int g = 0; g < nsteps; ++g) {
+    // this step's loads have landed once at most the later steps' are pending
+    wait_vmcnt_dyn<(kLeanRing - 1) * kLoads>(min(kLeanRing - 1, nsteps - 1 - g) * kLoads);
+    const u32x4* slot = reinterpret_cast<const u32x4*>(smem + (g % kLeanRing) * kLeanSlotBytes);
+#pragma unroll
+    for (int h = 0; h < kDK / 32; ++h) {
+      const int c = h * 4 + (lane >> 4);
+      bf16x8 a, b0, b1;
+      const u32x4 va = slot[dswz<8>(lane & 15, c)];
+      const u32x4 v0 = slot[dswz<8>(16 + (lane & 15), c)];
+      const u32x4 v1 = slot[dswz<8>(32 + (lane & 15), c)];
+      __builtin_memcpy(&a, &va, 16);
+      __builtin_memcpy(&b0, &v0, 16);
+      __builtin_memcpy(&b1, &v1, 16);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc1, 0, 0, 0);
+      // one slice's fragments live at a time (the register budget of a wave beside the tiles)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkmcnt0();  // the slot's reads are in registers before its refill
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (g + kLeanRing < nsteps) issue(g + kLeanRing);
+    if (++cst == nst) {  // the item's last step: epilogue
+      cst = 0;
+      const int it = first + cj * stride;
+      ++cj;
+      advance(wc, it);
+      const int c0 = (it - wc.base) * NC;
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) {
+        const int r = (lane >> 4) * 4 + jr;
+        if (r >= wc.n) continue;
+        const size_t orow = (size_t)(wc.r0 + r) * p.N;
+        const int col = c0 + (lane & 15);
+        if constexpr (GATED) {
+          static_cast<__bf16*>(p.out)[orow + col] = (__bf16)(silu(acc0[jr]) * acc1[jr]);
+        } else {
+          static_cast<float*>(p.out)[orow + col] = acc0[jr];
+          static_cast<float*>(p.out)[orow + col + 16] = acc1[jr];
+        }
+      }
+      acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1 = acc0;
+    }
+  }
 }
 
 template <int WF, bool GATED, int HWM, int HWN, int HRING, int HDK, int CWN, int CRING, int CDK>
@@ -1532,8 +1717,37 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
     pgu.split_info = pdn.split_info = reinterpret_cast<int32_t*>(tail);
     pgu.partial = pdn.partial = reinterpret_cast<float*>(tail + 256);
     if (a.wdt == MOE_BF16) {
-      st = launch_prefill<kBF16, true, 128, 64, 2, 64, 32, 4, 64>(pgu, dev, stream);
-      if (st == hipSuccess) st = launch_prefill<kBF16, false, 128, 64, 2, 64, 32, 4, 64>(pdn, dev, stream);
+      // The experts with <= kStreamMaxRows rows may go to ffn_lean_kernel on a second stream
+      // beside the large tiles (both kernels decide from the counts), if its workgroups fit in
+      // the LDS a prefill workgroup leaves.
+      const size_t lds_pre = std::max(dl_lds_bytes<kBF16, 128, 64, 2, 4, 2, 64>(pgu),
+                                      dl_lds_bytes<kBF16, 16, 32, 1, 8, kPrefillColdRing, 64>(pgu));
+      SideStream side;
+      const bool lean = lds_pair_fits(lds_pre, kLeanLdsBytes) && side_stream_for(stream, &side);
+      pgu.lean = pdn.lean = lean ? 1 : 0;
+      if (lean) {
+        // the side stream waits for what the caller's stream holds before this call
+        st = hipEventRecord(side.fork, stream);
+        if (st == hipSuccess) st = hipStreamWaitEvent(side.stream, side.fork, 0);
+        if (st != hipSuccess) return st;
+      }
+      st = launch_prefill<kBF16, true, 128, 64, 2, 64, 32, kPrefillColdRing, 64>(pgu, dev, stream);
+      if (st == hipSuccess && lean) {
+        ffn_lean_kernel<true, 256><<<dev.num_cus, kWave, kLeanLdsBytes, side.stream>>>(pgu, dev.num_cus, pgu.offsets);
+        st = hipGetLastError();
+      }
+      if (st == hipSuccess) st = launch_prefill<kBF16, false, 128, 64, 2, 64, 32, kPrefillColdRing, 64>(pdn, dev, stream);
+      if (st == hipSuccess && lean) {
+        // after the lean gate/up on its stream: it reads the h rows that launch wrote
+        ffn_lean_kernel<false, 256><<<dev.num_cus, kWave, kLeanLdsBytes, side.stream>>>(pdn, dev.num_cus, pdn.offsets);
+        st = hipGetLastError();
+      }
+      if (lean) {
+        // the caller's stream waits for the side stream's work (even after a failed launch)
+        const hipError_t j1 = hipEventRecord(side.join, side.stream);
+        const hipError_t j2 = j1 == hipSuccess ? hipStreamWaitEvent(stream, side.join, 0) : j1;
+        if (st == hipSuccess) st = j2;
+      }
     } else {
       st = launch_prefill<kFP8, true, 64, 64, 2, 128, 32, 3, 128>(pgu, dev, stream);
       if (st == hipSuccess) st = launch_prefill<kFP8, false, 64, 64, 2, 128, 32, 3, 128>(pdn, dev, stream);

@@ -36,6 +36,17 @@ struct DeviceInfo {
 // Queried once per device, cached (mutex-guarded) in api.cpp.
 hipError_t device_info(DeviceInfo* out);
 
+// A second stream that runs work beside the caller's stream inside one call, with the events
+// that fork it from and join it back to the caller's stream. One per (device, caller stream),
+// created on first use (default priority, non-blocking; also during a graph capture, with this
+// thread's capture mode relaxed for the creation) and kept until the process ends. Returns
+// false when it cannot be created (the caller then runs everything on its own stream).
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+bool side_stream_for(hipStream_t caller, SideStream* out);
+
 // ---------------------------------------------------------------------------------------
 // launchers (each enqueues on `stream` and returns the launch status)
 // ---------------------------------------------------------------------------------------

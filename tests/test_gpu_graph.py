@@ -52,9 +52,12 @@ def _poison(out):
     synth.CONFIGS["c2"],                                                   # decode: route, small permute, split-free tiles
     synth.tiny_config(T=5, d=1024, E=16, k=2, d_ff=512, act="bf16", w="bf16", zipf_s=1.0, seed=21),  # contraction split
     synth.tiny_config(T=700, d=192, E=40, k=2, d_ff=320, act="bf16", w="bf16", zipf_s=1.5, seed=13),  # prefill kernel, tail split
+    # prefill kernel with the small experts on the second stream (the fork and join are captured;
+    # the capture stream gets its own second stream, created during the capture)
+    synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16", zipf_s=2.0, seed=17),
     synth.tiny_config(T=128, d=512, E=64, k=4, d_ff=384, act="bf16", w="fp8_e4m3fn", zipf_s=1.0, seed=21),  # fp8 decode tiles
     synth.tiny_config(T=256, d=512, E=64, k=4, d_ff=384, act="bf16", w="fp8_e4m3fn", zipf_s=1.0, seed=21),  # fp8 prefill kernel
-], ids=["c2", "decode-split", "prefill", "fp8-decode", "fp8-prefill"])
+], ids=["c2", "decode-split", "prefill", "prefill-second-stream", "fp8-decode", "fp8-prefill"])
 def test_layer_graph_replay_matches_eager(dev, cfg):
     fn, out = _layer_fn(cfg, dev)
     fn()

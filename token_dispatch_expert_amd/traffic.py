@@ -83,3 +83,60 @@ def combine_bytes(T: int, k: int, d: int, out_bytes: int = 4) -> int:
     """y_sorted (fp32) rows read, flat_to_sorted and gates read, y written."""
     R = T * k
     return R * d * 4 + R * 8 + T * d * out_bytes
+
+
+def prefill_schedule_fills(counts, K: int, N: int, gated: bool, cus: int = 256, group_rows: int = 4,
+                           small_rows: int = 16, stream_cu_gbps: float = 30.0,
+                           tile_cu_tflops: float = 4.0) -> dict:
+    """A model of the L2 fills (bytes fetched past the L2) of one prefill-kernel GEMM launch.
+
+    It follows the large-tile schedule: experts with more than `small_rows` rows in 256-row tiles
+    (rows dealt in 16-row fragments), `cols` output columns per tile (128 gated, 256 plain), item
+    order by expert, then groups of `group_rows` row tiles with the column blocks outer; X
+    streaming CUs (the kernel's balance rule) leave cus - X ranks; each round's items go to the 8
+    XCDs in runs of consecutive items. Within a round an XCD fetches every distinct A tile (an
+    expert's row tile, rows x K x 2 bytes) and B tile (256 weight rows x K x 2 bytes) it needs
+    once over the whole contraction, and nothing outlives the round (a K-panel is MBs, the L2 per
+    XCD 4 MB). The streaming role reads its experts' weights once. bf16 operands."""
+    import math
+    cols = 128 if gated else 256
+    nt_per_expert = N // cols
+    w_bytes = (2 if gated else 1) * N * K * 2
+    hot = [(e, int(n)) for e, n in enumerate(counts) if n > small_rows]
+    n_small = sum(1 for n in counts if 0 < n <= small_rows)
+    tc = n_small * w_bytes / (stream_cu_gbps * 1e9)
+    th = sum(2 * math.ceil(n / 256) * 256 * K * (2 * N if gated else N) for _, n in hot) / (tile_cu_tflops * 1e12)
+    X = 0
+    if tc > 0:
+        X = int(cus * tc / (tc + th) / 8 + 0.5) * 8 if th > 0 else cus
+        X = max(X, min(8, cus))
+        if th > 0:
+            X = min(X, cus - 8)
+    ranks = cus - X
+    items = []
+    for e, n in hot:
+        mt_count = math.ceil(n / 256)
+        frags = math.ceil(n / 16)
+        q, rem = divmod(frags, mt_count)
+        tile_rows = []
+        for mt in range(mt_count):
+            first = 16 * (mt * q + min(mt, rem))
+            tile_rows.append(min(16 * (q + (1 if mt < rem else 0)), n - first))
+        for local in range(mt_count * nt_per_expert):
+            g = local // (group_rows * nt_per_expert)
+            gm = min(group_rows, mt_count - g * group_rows)
+            j = local - g * group_rows * nt_per_expert
+            items.append((e, g * group_rows + j % gm, j // gm, tile_rows[g * group_rows + j % gm]))
+    fills = 0
+    if ranks > 0:
+        for base in range(0, len(items), ranks):
+            n = min(ranks, len(items) - base)
+            run = math.ceil(n / 8)
+            for x in range(8):
+                its = items[base + x * run: base + min(n, (x + 1) * run)]
+                a_tiles = {(e, mt): r for e, mt, _, r in its}
+                b_tiles = {(e, nt) for e, _, nt, _ in its}
+                fills += sum(a_tiles.values()) * K * 2 + len(b_tiles) * 256 * K * 2
+    return {"streaming_cus": X, "tile_items": len(items), "tile_fills": fills,
+            "streamed": n_small * w_bytes, "fills": fills + n_small * w_bytes,
+            "algorithmic": sum(n for _, n in hot) * K * 2 + len(hot) * w_bytes + n_small * w_bytes}

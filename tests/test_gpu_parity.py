@@ -57,7 +57,7 @@ def run_full(cfg, dev, logits=None, x=None, plain_bar=True):
     return got, ref
 
 
-def run_sampled(cfg, dev, n_tokens, seed=0):
+def run_sampled(cfg, dev, n_tokens, seed=0, logits=None):
     """Full-size layer: routing/permutation in full, float outputs on a token sample that
     reaches every active expert, every row tile and every kernel role.
 
@@ -68,7 +68,8 @@ def run_sampled(cfg, dev, n_tokens, seed=0):
     y-level comparison with a bf16-h oracle is statistical at this size: the rare h element
     whose fp32 and fp64 values round to different bf16 neighbours moves its row's outputs by one
     bf16 unit of h, and over thousands of rows the largest such move exceeds 5e-3 of rms.)"""
-    logits, x = synth.make_routing_inputs(cfg)
+    lg0, x = synth.make_routing_inputs(cfg)
+    logits = lg0 if logits is None else logits
     ref_ids, ref_gates = oracle.route(logits, cfg.k)
     perm = oracle.permute(ref_ids, cfg.E)
     W = H.DeviceWeights(cfg, dev, experts=H.active_experts(perm["counts"]))
@@ -243,6 +244,30 @@ def test_prefill_small_experts_beside_tiles(dev, zipf, lean):
           flush=True)
     assert regime == [lean, lean]
     run_full(cfg, dev)
+
+
+def test_lean_kernel_every_small_count(dev):
+    # every count from 1 to 16 rows once, two empty experts, and four experts of 5,000 rows
+    # (enough tile work beside them for the rule to send the small ones to the lean kernel),
+    # interleaved so that the lean kernel's walker steps over large and empty experts
+    small = list(range(1, 17))
+    counts = []
+    for j, c in enumerate(small):
+        counts.append(c)
+        if j % 4 == 3:
+            counts.append(5000 if j < 15 else 0)
+    counts = [0] + counts + [5000]
+    E = len(counts)
+    assert sorted(c for c in counts if 0 < c <= 16) == small and counts.count(5000) == 4
+    owners = [[e] for e, c in enumerate(counts) for _ in range(c)]
+    np.random.default_rng(12).shuffle(owners)
+    cfg = synth.tiny_config(T=len(owners), d=256, E=E, k=1, d_ff=256, act="bf16", w="bf16", seed=12)
+    assert cfg.T * cfg.k >= 32 * cfg.E
+    assert _small_beside_large(np.array(counts), cfg.d, cfg.d_ff) == [True, True]
+    # 20,136 rows: the sampled check (every row of the small experts; the implementation's own h
+    # element by element, then its down projection at the fp32 bar), since a y-level comparison
+    # with the bf16-h oracle is a tail statistic at thousands of rows
+    run_sampled(cfg, dev, n_tokens=64, seed=12, logits=_onehot_logits(owners, E))
 
 
 @pytest.mark.parametrize("T", [24, 90])

@@ -1411,7 +1411,9 @@ __global__ __launch_bounds__(512) void ffn_prefill_kernel(TiledArgs p) {
 // Lean streaming kernel for the experts with 1..kStreamMaxRows rows of a prefill-sized bf16
 // launch, run on a second stream beside ffn_prefill_kernel so that every CU keeps its large
 // tiles: a large-tile workgroup leaves 32 VGPRs per SIMD and ~19.5 KB of LDS unused, and this
-// kernel's single-wave workgroups fit there (at most 32 VGPRs, kLeanRing * 6 KB of LDS). Each
+// kernel's single-wave workgroups fit there (a 32-VGPR budget, which the compiler meets with one
+// slice's fragments live at a time; kLeanRing * 6 KB of LDS; the host checks both against the
+// code objects before using it). Each
 // wave streams its items through a private ring of direct-to-LDS loads (no barriers; the waits
 // are its own load counts) that runs on across item boundaries. An item is (expert, 16 gate and
 // the same 16 up columns of h) or (expert, 32 columns of y); a 64-wide step loads the item's
@@ -1432,8 +1434,8 @@ constexpr int kPrefillColdRing = 4;  // the prefill kernel's streaming-role ring
 constexpr int kLeanSlotBytes = 6 * 1024;
 constexpr int kLeanLdsBytes = kLeanRing * kLeanSlotBytes;
 template <bool GATED, int HTM>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_num_vgpr(32))) void ffn_lean_kernel(TiledArgs p, int G,
-                                                                              const int32_t* __restrict__ offs) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_num_vgpr(32)))
+void ffn_lean_kernel(TiledArgs p, int G, const int32_t* __restrict__ offs) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x;
   {
@@ -1584,6 +1586,24 @@ static hipError_t launch_prefill(const TiledArgs& p, const DeviceInfo& dev, hipS
   return hipGetLastError();
 }
 
+// Whether a lean-kernel wave fits in the registers that two prefill-kernel waves leave on a SIMD
+// (512 per lane, allocated in units of 8), from the kernels' code objects; read once.
+static bool lean_regs_fit() {
+  static const bool fit = [] {
+    auto regs = [](const void* f) {
+      hipFuncAttributes a{};
+      return hipFuncGetAttributes(&a, f) == hipSuccess ? (int)align_up((size_t)a.numRegs, 8) : 1 << 20;
+    };
+    const int lean = std::max(regs(reinterpret_cast<const void*>(&ffn_lean_kernel<true, 256>)),
+                              regs(reinterpret_cast<const void*>(&ffn_lean_kernel<false, 256>)));
+    const int pre = std::max(
+        regs(reinterpret_cast<const void*>(&ffn_prefill_kernel<kBF16, true, 128, 64, 2, 64, 32, kPrefillColdRing, 64>)),
+        regs(reinterpret_cast<const void*>(&ffn_prefill_kernel<kBF16, false, 128, 64, 2, 64, 32, kPrefillColdRing, 64>)));
+    return 2 * pre + lean <= 512;
+  }();
+  return fit;
+}
+
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN, int RING = kRing, int DK = kDK,
           bool ASKIP = false>
 static hipError_t launch_tiled_dl(const TiledArgs& p, const DeviceInfo& dev, hipStream_t stream) {
@@ -1723,7 +1743,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
       const size_t lds_pre = std::max(dl_lds_bytes<kBF16, 128, 64, 2, 4, 2, 64>(pgu),
                                       dl_lds_bytes<kBF16, 16, 32, 1, 8, kPrefillColdRing, 64>(pgu));
       SideStream side;
-      const bool lean = lds_pair_fits(lds_pre, kLeanLdsBytes) && side_stream_for(stream, &side);
+      const bool lean = lds_pair_fits(lds_pre, kLeanLdsBytes) && lean_regs_fit() &&
+                        side_stream_for(stream, &side);
       pgu.lean = pdn.lean = lean ? 1 : 0;
       if (lean) {
         // the side stream waits for what the caller's stream holds before this call

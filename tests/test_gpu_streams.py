@@ -1,0 +1,57 @@
+"""The grouped FFN on several caller streams at once, with the small experts on the library's
+second stream (one per caller stream, forked from it and joined back inside the call).
+
+Each call's output is poisoned on its caller stream before the call and copied on that stream
+right after it, so a copy taken before the second stream's work has joined back would hold the
+poison or partial rows. Every copy must equal a reference computed alone on the default stream,
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_dispatch_expert_amd as moe
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return H.require_gpu()
+
+
+def test_grouped_ffn_on_two_caller_streams(dev):
+    # the routing of the lean-regime parity case: 10 experts with <= 16 rows beside large ones
+    cfg = synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16",
+                            zipf_s=2.0, seed=17)
+    logits, x = synth.make_routing_inputs(cfg)
+    ids, _ = oracle.route(logits, cfg.k)
+    perm = oracle.permute(ids, cfg.E)
+    W = H.DeviceWeights(cfg, dev, experts=H.active_experts(perm["counts"]))
+    xs = H.to_dev(oracle.gather_rows(x, perm["sorted_to_flat"], cfg.k), cfg.act, dev)
+    offs = torch.from_numpy(np.asarray(perm["offsets"], np.int32)).to(dev)
+    R = cfg.T * cfg.k
+    nws = moe.moe_ffn_workspace_size(R, cfg.E, cfg.d, cfg.d_ff, torch.bfloat16, torch.bfloat16)
+
+    ref = torch.full((R, cfg.d), float("nan"), device=dev)
+    moe.moe_grouped_ffn(xs, offs, W.gate, W.up, W.down, ref, moe.Workspace(nws, device=dev))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(ref).all())
+
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty(R, cfg.d, device=dev) for _ in streams]
+    wss = [moe.Workspace(nws, device=dev) for _ in streams]
+    copies = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for s, y, ws in zip(streams, outs, wss):
+            with torch.cuda.stream(s):
+                y.fill_(float("nan"))
+                moe.moe_grouped_ffn(xs, offs, W.gate, W.up, W.down, y, ws, stream=s)
+                copies.append(y.clone())
+    torch.cuda.synchronize()
+    for n, c in enumerate(copies):
+        assert torch.equal(c.view(torch.int32), ref.view(torch.int32)), f"copy {n} differs"

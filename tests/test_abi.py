@@ -137,6 +137,25 @@ def test_ffn_rejects_bad_arguments(lib):
     assert call(wsb=wsb - 1) == B.MOE_ERR_WORKSPACE
     assert call(rows=-1, ws=None) == B.MOE_ERR_INVALID_ARG
     assert call(wg=MIS, ws=None) == B.MOE_ERR_INVALID_ARG
+    # blocked bf16 weights: bf16 activations, d and d_ff multiples of 64, the bf16 workspace
+    assert lib.moe_ffn_workspace_size(rows, E, d, d_ff, B.MOE_BF16, B.MOE_BF16_BLOCKED) == wsb
+    assert call(wdt=B.MOE_BF16_BLOCKED, ws=None) == B.MOE_ERR_WORKSPACE          # accepted
+    assert call(wdt=B.MOE_BF16_BLOCKED, d_ff=320 + 8, ws=None) == B.MOE_ERR_UNSUPPORTED
+    assert call(wdt=B.MOE_BF16_BLOCKED, act=B.MOE_F32, ws=None) == B.MOE_ERR_UNSUPPORTED
+    assert call(wdt=B.MOE_BF16_BLOCKED, sg=P, ws=None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_block_weights_rejects_bad_arguments(lib):
+    # every case fails validation before anything is enqueued (no call here has valid arguments)
+    f = lib.moe_block_weights
+    big = 1 << 40  # an aligned address far from P
+    assert f(P, big, 0, 16, 128, None) == B.MOE_ERR_INVALID_ARG            # E < 1
+    assert f(P, big, 2, 12, 128, None) == B.MOE_ERR_INVALID_ARG            # N not /8
+    assert f(P, big, 2, 16, 96, None) == B.MOE_ERR_INVALID_ARG             # K not /64
+    assert f(None, big, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # null
+    assert f(MIS, big, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG          # misaligned
+    assert f(P, P + 64, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # overlapping
+    assert f(P, big, 1 << 16, 1 << 8, 1 << 8, None) == B.MOE_ERR_INVALID_ARG  # 2^32 elements
 
 
 def test_combine_and_layer_reject_bad_arguments(lib):

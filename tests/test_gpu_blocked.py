@@ -1,0 +1,81 @@
+"""bf16 weights in the MOE_BF16_BLOCKED layout (blocks of 8 rows x 64 contraction elements).
+
+moe_block_weights is checked against the layout's definition (a numpy reshape and transpose),
+and whole layers with blocked weights against the same layers with row-major weights: the
+arithmetic is the same, so every output must be bit-identical, on every kernel path that reads
+bf16 weights (decode-sized tiles, their contraction split, the prefill kernel's large tiles and
+streaming role, and the lean kernel on the second stream)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_dispatch_expert_amd as moe
+from token_dispatch_expert_amd.binding import layer_buffers
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return H.require_gpu()
+
+
+def _blocked_reference(w: np.ndarray) -> np.ndarray:
+    """[E, N, K] -> [E][N/8][K/64][8][64], flattened back to [E, N, K] storage."""
+    E, N, K = w.shape
+    return w.reshape(E, N // 8, 8, K // 64, 64).transpose(0, 1, 3, 2, 4).reshape(E, N, K)
+
+
+def test_block_weights_layout(dev):
+    rng = np.random.default_rng(3)
+    for E, N, K in ((1, 8, 64), (3, 24, 192), (2, 136, 320)):
+        bits = rng.integers(0, 1 << 16, size=(E, N, K), dtype=np.uint16)
+        src = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        dst = torch.full_like(src, float("nan"))
+        moe.moe_block_weights(src, dst)
+        torch.cuda.synchronize()
+        got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, _blocked_reference(bits)), (E, N, K)
+
+
+def _run(cfg, dev, W, blocked):
+    logits, x = synth.make_routing_inputs(cfg)
+    lg = torch.from_numpy(logits).to(dev)
+    xd = H.to_dev(x, cfg.act, dev)
+    out = layer_buffers(cfg.T, cfg.E, cfg.k, cfg.d, torch.bfloat16, device=dev)
+    ws = moe.Workspace(moe.moe_layer_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff,
+                                                    torch.bfloat16, torch.bfloat16), device=dev)
+    for t in out.values():
+        t.fill_(float("nan")) if t.is_floating_point() else t.fill_(-7)
+    ws.buf.fill_(0xFF)
+    gate, up, down = W
+    moe.moe_layer(lg, xd, gate, up, down, cfg.k, out, ws, weights_blocked=blocked)
+    torch.cuda.synchronize()
+    return {n: t.cpu() for n, t in out.items()}
+
+
+@pytest.mark.parametrize("cfg", [
+    synth.CONFIGS["c2"],                                                             # decode tiles
+    synth.tiny_config(T=5, d=1024, E=16, k=2, d_ff=512, act="bf16", w="bf16", zipf_s=1.0, seed=21),   # split
+    synth.tiny_config(T=700, d=192, E=40, k=2, d_ff=320, act="bf16", w="bf16", zipf_s=1.5, seed=13),  # prefill
+    synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16", zipf_s=0.9, seed=17),  # streaming role
+    synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16", zipf_s=2.0, seed=17),  # lean kernel
+], ids=["c2", "decode-split", "prefill", "prefill-streaming-role", "prefill-second-stream"])
+def test_blocked_layer_matches_row_major(dev, cfg):
+    logits, _ = synth.make_routing_inputs(cfg)
+    ids, _ = oracle.route(logits, cfg.k)
+    W = H.DeviceWeights(cfg, dev, experts=H.active_experts(np.bincount(ids.ravel(), minlength=cfg.E)))
+    blocked = []
+    for w in (W.gate, W.up, W.down):
+        b = torch.empty_like(w)
+        moe.moe_block_weights(w, b)
+        blocked.append(b)
+    ref = _run(cfg, dev, (W.gate, W.up, W.down), False)
+    got = _run(cfg, dev, tuple(blocked), True)
+    assert bool(torch.isfinite(ref["y"]).all())
+    for n in ref:
+        assert torch.equal(got[n].view(torch.uint8), ref[n].view(torch.uint8)), n

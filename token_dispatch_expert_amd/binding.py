@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libmoe.so"
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_BF16_BLOCKED = 0, 1, 2, 3
 
 _DTYPE_ENUM = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16,
                torch.float8_e4m3fn: MOE_FP8_E4M3FN, torch.uint8: MOE_FP8_E4M3FN}
@@ -28,6 +28,7 @@ ENTRY_POINTS = (
     "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_layer_workspace_size",
     "moe_layer", "moe_expert_capacity", "moe_permute_capped", "moe_layer_capped",
     "moe_route_gemm", "moe_route_gemm_workspace_size", "moe_permute_noalloc",
+    "moe_block_weights",
 )
 
 _lib = None
@@ -69,6 +70,7 @@ def load_library(path: str | None = None):
         "moe_route_gemm_workspace_size": ([I, I, I], S),
         "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "moe_permute_noalloc": ([P, I, P, I, I, I, I, P, P, P, P, P, P], I),
+        "moe_block_weights": ([P, P, I, I, I, P], I),
         "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
                               P, P, P, P, P, P, P, P, P, I, P, S, P], I),
     }
@@ -235,11 +237,17 @@ def moe_expert_capacity(T: int, E: int, k: int, factor_percent: int) -> int:
     return load_library().moe_expert_capacity(T, E, k, int(factor_percent))
 
 
-def _weights(w_gate, w_up, w_down, s_gate, s_up, s_down):
+def _weights(w_gate, w_up, w_down, s_gate, s_up, s_down, blocked=False):
+    """blocked: the bf16 weights are in the MOE_BF16_BLOCKED layout (see moe_block_weights); the
+    tensors keep their [E, d_ff, d] / [E, d, d_ff] shapes."""
     E, d_ff, d = w_gate.shape
     _need(w_up, w_gate.dtype, (E, d_ff, d), "w_up")
     _need(w_down, w_gate.dtype, (E, d, d_ff), "w_down")
     w_dt = _dt(w_gate, "w_gate")
+    if blocked:
+        if w_dt != MOE_BF16:
+            raise TypeError("blocked weights are bfloat16")
+        w_dt = MOE_BF16_BLOCKED
     if w_dt == MOE_FP8_E4M3FN:
         for s, shp, n in ((s_gate, (E, -(-d_ff // 128), -(-d // 128)), "s_gate"),
                           (s_up, (E, -(-d_ff // 128), -(-d // 128)), "s_up"),
@@ -250,10 +258,20 @@ def _weights(w_gate, w_up, w_down, s_gate, s_up, s_down):
     return E, d, d_ff, w_dt
 
 
+def moe_block_weights(src, dst, stream=None):
+    """dst [E, N, K] bf16 <- src [E, N, K] bf16 in the MOE_BF16_BLOCKED layout."""
+    if src.dim() != 3:
+        raise ValueError("src: expected [E, N, K]")
+    E, N, K = src.shape
+    _need(src, torch.bfloat16, (E, N, K), "src")
+    _need(dst, torch.bfloat16, (E, N, K), "dst")
+    _check(load_library().moe_block_weights(_ptr(src), _ptr(dst), E, N, K, _stream(stream)))
+
+
 def moe_grouped_ffn(x_sorted, offsets, w_gate, w_up, w_down, y_sorted, workspace: Workspace,
-                    s_gate=None, s_up=None, s_down=None, stream=None):
+                    s_gate=None, s_up=None, s_down=None, stream=None, weights_blocked=False):
     rows, d_x = x_sorted.shape
-    E, d, d_ff, w_dt = _weights(w_gate, w_up, w_down, s_gate, s_up, s_down)
+    E, d, d_ff, w_dt = _weights(w_gate, w_up, w_down, s_gate, s_up, s_down, weights_blocked)
     if d_x != d:
         raise ValueError("x_sorted and weights disagree on d")
     _need(offsets, torch.int32, (E + 1,), "offsets")
@@ -287,13 +305,15 @@ def moe_combine(y_sorted, flat_to_sorted, topk_gates, y, stream=None):
 
 
 def moe_layer(logits, x, w_gate, w_up, w_down, k: int, out: dict, workspace: Workspace,
-              s_gate=None, s_up=None, s_down=None, stream=None, capacity: int | None = None):
+              s_gate=None, s_up=None, s_down=None, stream=None, capacity: int | None = None,
+              weights_blocked=False):
     """out holds the caller's buffers: topk_ids, topk_gates, counts, offsets, sorted_to_flat,
     flat_to_sorted, x_sorted, y_sorted, y (see `layer_buffers`; y float32 or bfloat16).
-    capacity (optional): most kept assignments per expert (moe_layer_capped)."""
+    capacity (optional): most kept assignments per expert (moe_layer_capped).
+    weights_blocked: bf16 weights in the MOE_BF16_BLOCKED layout (moe_block_weights)."""
     T, E = logits.shape
     _need(logits, torch.float32, (T, E), "logits")
-    Ew, d, d_ff, w_dt = _weights(w_gate, w_up, w_down, s_gate, s_up, s_down)
+    Ew, d, d_ff, w_dt = _weights(w_gate, w_up, w_down, s_gate, s_up, s_down, weights_blocked)
     if Ew != E or x.shape != (T, d):
         raise ValueError("logits, x and weights disagree on T, E or d")
     R = T * k

@@ -136,11 +136,11 @@ moe_status_t check_ffn(const void* x_sorted, moe_dtype_t act, const int32_t* off
   if (act == MOE_F32) {
     if (wdt != MOE_F32) return MOE_ERR_UNSUPPORTED;
   } else if (act == MOE_BF16) {
-    if (wdt != MOE_BF16 && wdt != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+    if (wdt != MOE_BF16 && wdt != MOE_FP8_E4M3FN && wdt != MOE_BF16_BLOCKED) return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
-  const int mult = wdt == MOE_FP8_E4M3FN ? 128 : 8;
+  const int mult = wdt == MOE_FP8_E4M3FN ? 128 : (wdt == MOE_BF16_BLOCKED ? 64 : 8);
   if (d % mult != 0 || d_ff % mult != 0) return MOE_ERR_UNSUPPORTED;
   const long long wel = (long long)E * d * d_ff;
   if (!ok_ptr(x_sorted, (long long)rows * d, 16) || !ok_ptr(offsets, E + 1, 4) ||
@@ -302,6 +302,17 @@ moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const 
   moe::FfnArgs a{x_sorted, act_dtype, offsets, rows, E, d, d_ff, w_gate, w_up, w_down,
                  w_dtype, s_gate, s_up, s_down, y_sorted, workspace};
   return hip_status(moe::launch_grouped_ffn(a, dev, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_block_weights(const void* src, void* dst, int E, int N, int K, void* stream) {
+  if (E < 1 || N < 8 || K < 64 || N % 8 != 0 || K % 64 != 0) return MOE_ERR_INVALID_ARG;
+  const long long n = (long long)E * N * K;
+  if (n >= (long long)INT_MAX) return MOE_ERR_INVALID_ARG;
+  if (!ok_ptr(src, n, 16) || !ok_ptr(dst, n, 16)) return MOE_ERR_INVALID_ARG;
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + 2 * n && d0 < s0 + 2 * n) return MOE_ERR_INVALID_ARG;  // overlap
+  return hip_status(moe::launch_block_weights(src, dst, E, N, K, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_combine(const float* y_sorted, const int32_t* flat_to_sorted,

@@ -495,6 +495,9 @@ struct TiledArgs {
   // prefill: 1 when ffn_lean_kernel runs beside this launch on a second stream and may take the
   // experts with at most kStreamMaxRows rows (both kernels decide from the counts alike)
   int lean = 0;
+  // bf16 weights in the MOE_BF16_BLOCKED layout ([N/8][K/64][8][64]); only read by the bf16
+  // direct-to-LDS tiles with 64-wide steps and the lean kernel
+  int wblk = 0;
 };
 
 template <int WF, bool GATED, int WM, int WN, int WGM, int WGN>
@@ -876,6 +879,7 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
                 "decode contraction split: bf16 weights, tiles of at most 64 x 128");
   constexpr bool F8 = WF == kFP8;
   constexpr int WB = F8 ? 1 : 2;                        // weight bytes per element
+  constexpr bool BLKOK = WF == kBF16 && DK == 64;        // shapes that read blocked weights
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
   constexpr int TM = WGM * WM, TN = WGN * WN;
   constexpr int MF = WM / 16, NF = WN / 16;
@@ -1092,12 +1096,18 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
         const int q = wave * 64 + lane;
         const int t = q / CPRB, c = dswz<CPRB>(t, q % CPRB) - t * CPRB;
         b_lane = b_row(t) * p.K * WB + c * 16;
+        // blocked weights: a load instruction's 8 rows (b_row(t) & 7 is this lane's row among
+        // them, the first is a multiple of 8) are one 1 KB block per step, row r at r * 128
+        if constexpr (BLKOK)
+          if (p.wblk) b_lane = (b_row(t) & ~7) * p.K * 2 + (b_row(t) & 7) * 128 + c * 16;
       }
       const int t0w = wave * RPB;  // first B row of this wave's instruction 0 (wave-uniform)
+      // bytes between steps in a B row: DK elements, or one 1 KB block (blocked weights)
+      const int kbstep = (BLKOK && p.wblk) ? 1024 : DK * WB;
 
       auto issue = [&](int st) __attribute__((always_inline)) {
         u32x4* slot = ring + (st % RING) * STAGE;
-        const int ka = st * DK * 2, kb = st * DK * WB;
+        const int ka = st * DK * 2, kb = st * kbstep;
   #pragma unroll
         for (int i = 0; i < AIW; ++i)
           if (loads_a && (!ASKIP || (wave + i * NW) * RPA < nrows))
@@ -1485,6 +1495,10 @@ void ffn_lean_kernel(TiledArgs p, int G, const int32_t* __restrict__ offs) {
   const int c1s = (lane & 7) ^ (((8 + lr) >> 1) & 7);    // rows 8..15
   const int off0 = lr * p.K * 2 + c0s * 16, off1 = lr * p.K * 2 + c1s * 16;
   const int row8 = 8 * p.K * 2;                          // bytes of 8 operand rows
+  // weight loads: the same, or in blocked weights row lr of the 8-row block at lr * 128, 1 KB
+  // per step
+  const int boff0 = p.wblk ? lr * 128 + c0s * 16 : off0, boff1 = p.wblk ? lr * 128 + c1s * 16 : off1;
+  const int bstep = p.wblk ? 1024 : kDK * 2;
 
   // issue side: the next step to load, as (item index j of this wave, step); compute side alike
   Walker wi{0, 0, 0, 0}, wc{0, 0, 0, 0};
@@ -1503,14 +1517,14 @@ void ffn_lean_kernel(TiledArgs p, int G, const int32_t* __restrict__ offs) {
     const __amdgpu_buffer_rsrc_t rB2 = GATED ? __builtin_amdgcn_make_buffer_rsrc(
         (void*)(static_cast<const uint8_t*>(p.W2) + (size_t)wi.e * wstride + wcol), (short)0, (int)bext, kBufferWord3) : rB1;
     u32x4* slot = reinterpret_cast<u32x4*>(smem + (g % kLeanRing) * kLeanSlotBytes);
-    const int ks = ist * kDK * 2;
+    const int ks = ist * kDK * 2, kw = ist * bstep;
     // slot rows: 0..15 activations, 16..31 gate (or weight rows 0..15), 32..47 up (or 16..31)
     buffer_load_lds16(rA, slot + 0 * 64, off0, ks);
     buffer_load_lds16(rA, slot + 1 * 64, off1, row8 + ks);
-    buffer_load_lds16<kNonTemporal>(rB1, slot + 2 * 64, off0, ks);
-    buffer_load_lds16<kNonTemporal>(rB1, slot + 3 * 64, off1, row8 + ks);
-    buffer_load_lds16<kNonTemporal>(rB2, slot + 4 * 64, off0, (GATED ? 0 : 2 * row8) + ks);
-    buffer_load_lds16<kNonTemporal>(rB2, slot + 5 * 64, off1, (GATED ? 0 : 2 * row8) + row8 + ks);
+    buffer_load_lds16<kNonTemporal>(rB1, slot + 2 * 64, boff0, kw);
+    buffer_load_lds16<kNonTemporal>(rB1, slot + 3 * 64, boff1, row8 + kw);
+    buffer_load_lds16<kNonTemporal>(rB2, slot + 4 * 64, boff0, (GATED ? 0 : 2 * row8) + kw);
+    buffer_load_lds16<kNonTemporal>(rB2, slot + 5 * 64, boff1, (GATED ? 0 : 2 * row8) + row8 + kw);
     if (++ist == nst) { ist = 0; ++ij; }
   };
   constexpr int kLoads = 6;  // load instructions per step
@@ -1665,6 +1679,7 @@ static size_t tail_partial_bytes(moe_dtype_t wdt) {
 }
 
 size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
+  if (wdt == MOE_BF16_BLOCKED) wdt = MOE_BF16;  // the same kernels and workspace
   const size_t hb = act == MOE_F32 ? 4 : 2;
   const size_t h = align_up((size_t)rows * d_ff * hb, 256);
   if (uses_split(rows, E, d, d_ff, act, wdt)) return h + kPartialBytes;
@@ -1695,8 +1710,13 @@ static hipError_t launch_split(TiledArgs p, const DeviceInfo& dev, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream) {
-  if (a.rows == 0) return hipSuccess;
+hipError_t launch_grouped_ffn(const FfnArgs& a_in, const DeviceInfo& dev, hipStream_t stream) {
+  if (a_in.rows == 0) return hipSuccess;
+  // blocked bf16 weights run the bf16 kernels with the blocked addressing (validated: d and d_ff
+  // multiples of 64, so every bf16 tiled path below reads them, none of the streaming kernel's)
+  FfnArgs a = a_in;
+  const int wblk = a.wdt == MOE_BF16_BLOCKED ? 1 : 0;
+  if (wblk) a.wdt = MOE_BF16;
   // Which kernel takes which expert (decided per expert on the device from its row count):
   //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
   //  - decode-sized batches (T*k < 32*E with bf16 weights, T*k <= 8*E with fp8 weights): the
@@ -1720,6 +1740,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
                 a.E, a.d, a.d_ff, a.rows, small};
   TiledArgs tdn{a.h, a.w_down, nullptr, a.s_down, nullptr, a.y_sorted, a.offsets,
                 a.E, a.d_ff, a.d, a.rows, small};
+  tgu.wblk = tdn.wblk = wblk;
   // the fp8 direct-to-LDS kernel keeps an item's scale rows in LDS: 4 x 2 x K/128 floats
   const bool fp8_dl = big && a.d <= kFp8DlMaxK && a.d_ff <= kFp8DlMaxK;
   hipError_t st = hipSuccess;
@@ -1812,6 +1833,29 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream
          : tall       ? launch_tiled<kFP8, false, 128, 64, 2, 2>(tdn, dev, stream)
                       : launch_tiled<kFP8, false, 64, 64, 2, 2>(tdn, dev, stream);
   return st;
+}
+
+// MOE_BF16_BLOCKED weights from row-major ones: one thread per 16-byte piece (8 elements) of the
+// destination, in destination order, so the stores are contiguous and each source row piece is
+// read by one thread.
+__global__ __launch_bounds__(256) void block_weights_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                            int N, int K, long long pieces) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  // destination piece i: (e, n/8, k/64) block, row n%8 of it, 8-element piece c of that row
+  const int c = (int)(i & 7), r = (int)((i >> 3) & 7);
+  const long long blk = i >> 6;                  // (e * (N/8) + n/8) * (K/64) + k/64
+  const int kb = (int)(blk % (K / 64));
+  const long long row = blk / (K / 64) * 8 + r;  // e * N + n
+  dst[i] = src[(row * K + (long long)kb * 64 + c * 8) / 8];
+}
+
+hipError_t launch_block_weights(const void* src, void* dst, int E, int N, int K, hipStream_t stream) {
+  const long long pieces = (long long)E * N * K / 8;
+  const unsigned grid = (unsigned)((pieces + 255) / 256);
+  block_weights_kernel<<<grid, 256, 0, stream>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
+                                                 N, K, pieces);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -207,7 +207,7 @@ size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_
  *     ((e*(N/8) + n/8) * (K/64) + k/64) * 512 + (n%8) * 64 + k%64.
  * Weights are prepared once (at load time); a bit copy, no arithmetic.
  *   src, dst  [E*N*K] bf16 device buffers, not overlapping; E >= 1, N a multiple of 8, K of 64,
- *             E*N*K < 2^31.
+ *             N*K < 2^30 (each matrix under 2 GiB), E*N*K < 2^40.
  */
 moe_status_t moe_block_weights(const void* src, void* dst, int E, int N, int K, void* stream);
 

@@ -155,7 +155,8 @@ def test_block_weights_rejects_bad_arguments(lib):
     assert f(None, big, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # null
     assert f(MIS, big, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG          # misaligned
     assert f(P, P + 64, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # overlapping
-    assert f(P, big, 1 << 16, 1 << 8, 1 << 8, None) == B.MOE_ERR_INVALID_ARG  # 2^32 elements
+    assert f(P, big, 1, 1 << 15, 1 << 15, None) == B.MOE_ERR_INVALID_ARG   # a 2 GiB matrix
+    assert f(P, big, 1 << 20, 1 << 10, 1 << 10, None) == B.MOE_ERR_INVALID_ARG  # 2^40 elements
 
 
 def test_combine_and_layer_reject_bad_arguments(lib):

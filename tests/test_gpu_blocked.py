@@ -42,6 +42,28 @@ def test_block_weights_layout(dev):
         assert np.array_equal(got, _blocked_reference(bits)), (E, N, K)
 
 
+def test_block_weights_beyond_2g_elements(dev):
+    # a whole [E, N, K] tensor of more than 2^31 elements (the DeepSeek-V3 expert shape): every
+    # element checked by the index formula at sampled positions and over the last block
+    E, N, K = 147, 2048, 7168
+    assert E * N * K > 2 ** 31
+    g = torch.Generator(device=dev).manual_seed(5)
+    src = torch.randint(-32768, 32767, (E, N, K), dtype=torch.int16, device=dev, generator=g)
+    dst = torch.empty_like(src)
+    moe.moe_block_weights(src.view(torch.bfloat16), dst.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    e = torch.from_numpy(rng.integers(0, E, 4096)).to(dev)
+    n = torch.from_numpy(rng.integers(0, N, 4096)).to(dev)
+    k = torch.from_numpy(rng.integers(0, K, 4096)).to(dev)
+    e = torch.cat([e, torch.full((512,), E - 1, device=dev)])
+    n = torch.cat([n, (N - 8 + torch.arange(512, device=dev) // 64)])
+    k = torch.cat([k, (K - 64 + torch.arange(512, device=dev) % 64)])
+    pos = ((e * (N // 8) + n // 8) * (K // 64) + k // 64) * 512 + (n % 8) * 64 + k % 64
+    assert torch.equal(dst.view(-1)[pos], src[e, n, k])
+    del src, dst
+
+
 def _run(cfg, dev, W, blocked):
     logits, x = synth.make_routing_inputs(cfg)
     lg = torch.from_numpy(logits).to(dev)

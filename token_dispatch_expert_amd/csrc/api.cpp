@@ -306,8 +306,9 @@ moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const 
 
 moe_status_t moe_block_weights(const void* src, void* dst, int E, int N, int K, void* stream) {
   if (E < 1 || N < 8 || K < 64 || N % 8 != 0 || K % 64 != 0) return MOE_ERR_INVALID_ARG;
+  if ((long long)N * K >= (1LL << 30)) return MOE_ERR_INVALID_ARG;  // one matrix under 2 GiB
   const long long n = (long long)E * N * K;
-  if (n >= (long long)INT_MAX) return MOE_ERR_INVALID_ARG;
+  if (n >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
   if (!ok_ptr(src, n, 16) || !ok_ptr(dst, n, 16)) return MOE_ERR_INVALID_ARG;
   const char* s0 = static_cast<const char*>(src);
   const char* d0 = static_cast<const char*>(dst);

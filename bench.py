@@ -15,9 +15,9 @@ resident in HBM. Prints ONE JSON line on stdout (progress goes to stderr):
 
 Workloads (--config, default c4 = the DeepSeek-V3-shaped prefill layer, T=8192, the largest
 workload that the metric is quoted on; c2/c3 are the decode shapes, c5 the fp8-weight prefill):
-c1..c5 as in synth.CONFIGS. bf16 weights are put into the blocked layout (MOE_BF16_BLOCKED, by
-moe_block_weights) once before anything is timed, as a caller would at load time;
---row-major-weights keeps them row-major. Other modes: --calibrate-copy runs a plain device copy of
+c1..c5 as in synth.CONFIGS. bf16 and fp8 weights are put into their blocked layout
+(MOE_BF16_BLOCKED / MOE_FP8_E4M3FN_BLOCKED, by moe_block_weights) once before anything is timed,
+as a caller would at load time; --row-major-weights keeps them row-major. Other modes: --calibrate-copy runs a plain device copy of
 known size, the reference for scaling the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
@@ -423,7 +423,7 @@ def main() -> int:
                          "robustness runs of the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row-major-weights", action="store_true",
-                    help="keep bf16 weights row-major instead of the blocked layout")
+                    help="keep the weights row-major instead of the blocked layout")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--capacity-sweep", action="store_true",
                     help="layer tokens/s and drop rate for capacity factors 1.0..2.0")
@@ -496,10 +496,11 @@ def main() -> int:
         if e % 32 == 31:
             log(f"weights: {e + 1}/{E} experts generated and uploaded")
     torch.cuda.synchronize()
-    # bf16 weights go into the blocked layout once, before anything is timed (weights are
-    # prepared at load time); the naive baselines use the weights as plain torch matrices
-    blocked = (cfg.w == "bf16" and d % 64 == 0 and d_ff % 64 == 0 and not args.row_major_weights
-               and not args.naive_baselines)
+    # bf16 and fp8 weights go into their blocked layout once, before anything is timed (weights
+    # are prepared at load time); the naive baselines use the weights as plain torch matrices
+    blockable = ((cfg.w == "bf16" and d % 64 == 0 and d_ff % 64 == 0) or
+                 (cfg.w == "fp8_e4m3fn" and d <= 65536 and d_ff <= 65536))
+    blocked = blockable and not args.row_major_weights and not args.naive_baselines
     if blocked:
         for n in ("gate", "up", "down"):
             b = torch.empty_like(W[n])
@@ -623,7 +624,7 @@ def main() -> int:
         "data": "synthetic (seeded: Zipf-biased N(0,1) router logits, N(0,1) x, N(0,1/fan_in) weights)",
         "config": {"workload": f"{cfg.name}: {cfg.note}", "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff,
                    "activations": cfg.act, "weights": cfg.w,
-                   "weight_layout": "blocked 8x64" if blocked else "row-major",
+                   "weight_layout": "blocked (8 rows x 128 bytes)" if blocked else "row-major",
                    "zipf_s": cfg.zipf_s, "seed": cfg.seed,
                    "active_experts": active, "max_rows_per_expert": int(counts.max())},
         "roofline": roof,

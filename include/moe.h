@@ -39,12 +39,14 @@
  *
  * Number formats (moe_dtype_t): fp32, bf16, and OCP fp8 e4m3fn (1 sign, 4 exponent bits with
  * bias 7, 3 mantissa bits, no infinities, max 448) for weights only; and, for weights only,
- * MOE_BF16_BLOCKED: bf16 values with each [N, K] matrix (K its contraction axis) stored as
- * [N/8][K/64][8][64], i.e. blocks of 8 rows x 64 contraction elements, each block 1 KB
- * contiguous (moe_block_weights writes it from the row-major layout). The grouped FFN's tiles
- * load a step of 8 weight rows x 64 elements at a time, so in this layout each load reads one
- * contiguous kilobyte instead of 128 bytes of each of 8 rows 2*K bytes apart; the results are
- * bit-identical to MOE_BF16 with the same weight values.
+ * MOE_BF16_BLOCKED and MOE_FP8_E4M3FN_BLOCKED: bf16 / fp8 e4m3fn values with each [N, K] matrix
+ * (K its contraction axis) stored in blocks of 8 rows x 128 bytes (64 bf16 or 128 fp8
+ * contraction elements), each block 1 KB contiguous: [N/8][K/64][8][64] for bf16,
+ * [N/8][K/128][8][128] for fp8 (moe_block_weights writes them from the row-major layout). The
+ * grouped FFN's tiles load a step of 8 weight rows x 128 bytes at a time, so in these layouts
+ * each load reads one contiguous kilobyte instead of 128 bytes of each of 8 rows a row apart;
+ * the results are bit-identical to the row-major formats with the same weight values (fp8
+ * block scales keep their layout).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -64,7 +66,13 @@ typedef enum {
   MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3FN = 2, MOE_BF16_BLOCKED = 3 } moe_dtype_t;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3FN = 2,
+  MOE_BF16_BLOCKED = 3,       /* weights only */
+  MOE_FP8_E4M3FN_BLOCKED = 4  /* weights only */
+} moe_dtype_t;
 
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
@@ -201,15 +209,18 @@ size_t moe_ffn_workspace_size(int rows, int E, int d, int d_ff, moe_dtype_t act_
                               moe_dtype_t w_dtype);
 
 /*
- * moe_block_weights - copy bf16 weights from the row-major layout of moe_grouped_ffn
- * ([E, N, K], contraction axis K contiguous) into the MOE_BF16_BLOCKED layout
- * ([E][N/8][K/64][8][64]): element (e, n, k) goes to
- *     ((e*(N/8) + n/8) * (K/64) + k/64) * 512 + (n%8) * 64 + k%64.
+ * moe_block_weights - copy weights from the row-major layout of moe_grouped_ffn ([E, N, K],
+ * contraction axis K contiguous) into the blocked layout of the same format: with B = 64
+ * (w_dtype MOE_BF16, giving MOE_BF16_BLOCKED) or B = 128 (MOE_FP8_E4M3FN, giving
+ * MOE_FP8_E4M3FN_BLOCKED) contraction elements per block row, element (e, n, k) goes to
+ *     ((e*(N/8) + n/8) * (K/B) + k/B) * 8*B + (n%8) * B + k%B.
  * Weights are prepared once (at load time); a bit copy, no arithmetic.
- *   src, dst  [E*N*K] bf16 device buffers, not overlapping; E >= 1, N a multiple of 8, K of 64,
- *             N*K < 2^30 (each matrix under 2 GiB), E*N*K < 2^40.
+ *   src, dst  [E*N*K] device buffers in w_dtype, not overlapping; E >= 1, N a multiple of 8, K
+ *             of B, each matrix under 2 GiB, E*N*K < 2^40. Other w_dtype values give
+ *             MOE_ERR_UNSUPPORTED.
  */
-moe_status_t moe_block_weights(const void* src, void* dst, int E, int N, int K, void* stream);
+moe_status_t moe_block_weights(const void* src, void* dst, moe_dtype_t w_dtype, int E, int N, int K,
+                               void* stream);
 
 /*
  * moe_grouped_ffn - every expert's SwiGLU FFN over its contiguous rows, all experts in one
@@ -227,9 +238,10 @@ moe_status_t moe_block_weights(const void* src, void* dst, int E, int N, int K, 
  *   w_gate, w_up [E, d_ff, d] in w_dtype; w_down [E, d, d_ff] in w_dtype. Each matrix is
  *             stored with its contraction axis contiguous (the transpose of the math-side
  *             Wg, Wu [d, d_ff] and Wd [d_ff, d]).
- *   w_dtype   MOE_F32 with act MOE_F32; MOE_BF16, MOE_BF16_BLOCKED (each of the E matrices
- *             of w_gate, w_up, w_down in the blocked layout above; d and d_ff multiples of 64)
- *             or MOE_FP8_E4M3FN with act MOE_BF16.
+ *   w_dtype   MOE_F32 with act MOE_F32; MOE_BF16, MOE_FP8_E4M3FN, MOE_BF16_BLOCKED (each of the
+ *             E matrices of w_gate, w_up, w_down in the blocked layout above; d and d_ff
+ *             multiples of 64) or MOE_FP8_E4M3FN_BLOCKED (d and d_ff at most 65536) with act
+ *             MOE_BF16.
  *   s_gate, s_up [E, ceil(d_ff/128), ceil(d/128)], s_down [E, ceil(d/128), ceil(d_ff/128)]
  *             fp32 per-128x128-block scales of the stored matrices (fp8 only, else NULL):
  *             the weight value is code * scale of its block.

@@ -143,20 +143,29 @@ def test_ffn_rejects_bad_arguments(lib):
     assert call(wdt=B.MOE_BF16_BLOCKED, d_ff=320 + 8, ws=None) == B.MOE_ERR_UNSUPPORTED
     assert call(wdt=B.MOE_BF16_BLOCKED, act=B.MOE_F32, ws=None) == B.MOE_ERR_UNSUPPORTED
     assert call(wdt=B.MOE_BF16_BLOCKED, sg=P, ws=None) == B.MOE_ERR_INVALID_ARG
+    # blocked fp8: d and d_ff multiples of 128 and at most 65536, scales required
+    assert call(wdt=B.MOE_FP8_E4M3FN_BLOCKED, d_ff=512, ws=None) == B.MOE_ERR_INVALID_ARG   # no scales
+    assert call(wdt=B.MOE_FP8_E4M3FN_BLOCKED, d_ff=320, ws=None) == B.MOE_ERR_UNSUPPORTED
+    assert call(wdt=B.MOE_FP8_E4M3FN_BLOCKED, d=65536 + 128, ws=None) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_block_weights_rejects_bad_arguments(lib):
     # every case fails validation before anything is enqueued (no call here has valid arguments)
     f = lib.moe_block_weights
     big = 1 << 40  # an aligned address far from P
-    assert f(P, big, 0, 16, 128, None) == B.MOE_ERR_INVALID_ARG            # E < 1
-    assert f(P, big, 2, 12, 128, None) == B.MOE_ERR_INVALID_ARG            # N not /8
-    assert f(P, big, 2, 16, 96, None) == B.MOE_ERR_INVALID_ARG             # K not /64
-    assert f(None, big, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # null
-    assert f(MIS, big, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG          # misaligned
-    assert f(P, P + 64, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # overlapping
-    assert f(P, big, 1, 1 << 15, 1 << 15, None) == B.MOE_ERR_INVALID_ARG   # a 2 GiB matrix
-    assert f(P, big, 1 << 20, 1 << 10, 1 << 10, None) == B.MOE_ERR_INVALID_ARG  # 2^40 elements
+    bf, f8 = B.MOE_BF16, B.MOE_FP8_E4M3FN
+    assert f(P, big, B.MOE_F32, 2, 16, 128, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(P, big, B.MOE_BF16_BLOCKED, 2, 16, 128, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(P, big, bf, 0, 16, 128, None) == B.MOE_ERR_INVALID_ARG            # E < 1
+    assert f(P, big, bf, 2, 12, 128, None) == B.MOE_ERR_INVALID_ARG            # N not /8
+    assert f(P, big, bf, 2, 16, 96, None) == B.MOE_ERR_INVALID_ARG             # K not /64
+    assert f(P, big, f8, 2, 16, 192, None) == B.MOE_ERR_INVALID_ARG            # fp8 K not /128
+    assert f(None, big, bf, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # null
+    assert f(MIS, big, bf, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG          # misaligned
+    assert f(P, P + 64, bf, 2, 16, 128, None) == B.MOE_ERR_INVALID_ARG         # overlapping
+    assert f(P, big, bf, 1, 1 << 15, 1 << 15, None) == B.MOE_ERR_INVALID_ARG   # a 2 GiB matrix
+    assert f(P, big, f8, 1, 1 << 16, 1 << 15, None) == B.MOE_ERR_INVALID_ARG   # a 2 GiB fp8 matrix
+    assert f(P, big, bf, 1 << 20, 1 << 10, 1 << 10, None) == B.MOE_ERR_INVALID_ARG  # 2^40 elements
 
 
 def test_combine_and_layer_reject_bad_arguments(lib):

@@ -1,10 +1,13 @@
-"""bf16 weights in the MOE_BF16_BLOCKED layout (blocks of 8 rows x 64 contraction elements).
+"""Weights in the blocked layouts (8 rows x 128 bytes per block: 64 bf16 or 128 fp8 elements).
 
-moe_block_weights is checked against the layout's definition (a numpy reshape and transpose),
-and whole layers with blocked weights against the same layers with row-major weights: the
-arithmetic is the same, so every output must be bit-identical, on every kernel path that reads
-bf16 weights (decode-sized tiles, their contraction split, the prefill kernel's large tiles and
-streaming role, and the lean kernel on the second stream)."""
+moe_block_weights is checked against the layouts' definition (a numpy reshape and transpose),
+and whole layers with blocked weights against the same layers with row-major weights: where the
+same kernels run, the arithmetic is the same, so every output must be bit-identical, on every
+kernel path that reads bf16 weights (decode-sized tiles, their contraction split, the prefill
+kernel's large tiles and streaming role, and the lean kernel on the second stream) and fp8
+weights (decode-sized and prefill tiles). The smallest fp8 launches, whose row-major weights
+stream their few-row experts on another kernel (another summation order), are checked against
+the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -24,10 +27,10 @@ def dev():
     return H.require_gpu()
 
 
-def _blocked_reference(w: np.ndarray) -> np.ndarray:
-    """[E, N, K] -> [E][N/8][K/64][8][64], flattened back to [E, N, K] storage."""
+def _blocked_reference(w: np.ndarray, B: int) -> np.ndarray:
+    """[E, N, K] -> [E][N/8][K/B][8][B], flattened back to [E, N, K] storage."""
     E, N, K = w.shape
-    return w.reshape(E, N // 8, 8, K // 64, 64).transpose(0, 1, 3, 2, 4).reshape(E, N, K)
+    return w.reshape(E, N // 8, 8, K // B, B).transpose(0, 1, 3, 2, 4).reshape(E, N, K)
 
 
 def test_block_weights_layout(dev):
@@ -39,7 +42,15 @@ def test_block_weights_layout(dev):
         moe.moe_block_weights(src, dst)
         torch.cuda.synchronize()
         got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert np.array_equal(got, _blocked_reference(bits)), (E, N, K)
+        assert np.array_equal(got, _blocked_reference(bits, 64)), (E, N, K)
+    for E, N, K in ((1, 8, 128), (3, 24, 384), (2, 136, 640)):
+        codes = rng.integers(0, 256, size=(E, N, K), dtype=np.uint8)
+        src = torch.from_numpy(codes).to(dev).view(torch.float8_e4m3fn)
+        dst = torch.zeros_like(src.view(torch.uint8)).view(torch.float8_e4m3fn)
+        moe.moe_block_weights(src, dst)
+        torch.cuda.synchronize()
+        got = dst.view(torch.uint8).cpu().numpy()
+        assert np.array_equal(got, _blocked_reference(codes, 128)), (E, N, K)
 
 
 def test_block_weights_beyond_2g_elements(dev):
@@ -70,12 +81,12 @@ def _run(cfg, dev, W, blocked):
     xd = H.to_dev(x, cfg.act, dev)
     out = layer_buffers(cfg.T, cfg.E, cfg.k, cfg.d, torch.bfloat16, device=dev)
     ws = moe.Workspace(moe.moe_layer_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff,
-                                                    torch.bfloat16, torch.bfloat16), device=dev)
+                                                    torch.bfloat16, H.W_TORCH[cfg.w]), device=dev)
     for t in out.values():
         t.fill_(float("nan")) if t.is_floating_point() else t.fill_(-7)
     ws.buf.fill_(0xFF)
-    gate, up, down = W
-    moe.moe_layer(lg, xd, gate, up, down, cfg.k, out, ws, weights_blocked=blocked)
+    gate, up, down, skw = W
+    moe.moe_layer(lg, xd, gate, up, down, cfg.k, out, ws, weights_blocked=blocked, **skw)
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in out.items()}
 
@@ -86,8 +97,20 @@ def _run(cfg, dev, W, blocked):
     synth.tiny_config(T=700, d=192, E=40, k=2, d_ff=320, act="bf16", w="bf16", zipf_s=1.5, seed=13),  # prefill
     synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16", zipf_s=0.9, seed=17),  # streaming role
     synth.tiny_config(T=4096, d=512, E=128, k=4, d_ff=384, act="bf16", w="bf16", zipf_s=2.0, seed=17),  # lean kernel
-], ids=["c2", "decode-split", "prefill", "prefill-streaming-role", "prefill-second-stream"])
+    synth.tiny_config(T=128, d=512, E=64, k=4, d_ff=384, act="bf16", w="fp8_e4m3fn", zipf_s=1.0, seed=21),  # fp8 decode
+    synth.tiny_config(T=256, d=512, E=64, k=4, d_ff=384, act="bf16", w="fp8_e4m3fn", zipf_s=1.0, seed=21),  # fp8 prefill
+], ids=["c2", "decode-split", "prefill", "prefill-streaming-role", "prefill-second-stream",
+        "fp8-decode", "fp8-prefill"])
 def test_blocked_layer_matches_row_major(dev, cfg):
+    W, blocked = _weights_both(cfg, dev)
+    ref = _run(cfg, dev, (W.gate, W.up, W.down, W.kwargs()), False)
+    got = _run(cfg, dev, blocked, True)
+    assert bool(torch.isfinite(ref["y"]).all())
+    for n in ref:
+        assert torch.equal(got[n].view(torch.uint8), ref[n].view(torch.uint8)), n
+
+
+def _weights_both(cfg, dev):
     logits, _ = synth.make_routing_inputs(cfg)
     ids, _ = oracle.route(logits, cfg.k)
     W = H.DeviceWeights(cfg, dev, experts=H.active_experts(np.bincount(ids.ravel(), minlength=cfg.E)))
@@ -96,8 +119,19 @@ def test_blocked_layer_matches_row_major(dev, cfg):
         b = torch.empty_like(w)
         moe.moe_block_weights(w, b)
         blocked.append(b)
-    ref = _run(cfg, dev, (W.gate, W.up, W.down), False)
-    got = _run(cfg, dev, tuple(blocked), True)
-    assert bool(torch.isfinite(ref["y"]).all())
-    for n in ref:
-        assert torch.equal(got[n].view(torch.uint8), ref[n].view(torch.uint8)), n
+    return W, (*blocked, W.kwargs())
+
+
+def test_blocked_fp8_smallest_launch_against_oracle(dev):
+    # a decode step of 5 tokens: with row-major fp8 weights the few-row experts stream on the
+    # kernel that splits each item's contraction over its waves; blocked weights take the tiles
+    cfg = synth.tiny_config(T=5, d=1024, E=16, k=2, d_ff=512, act="bf16", w="fp8_e4m3fn",
+                            zipf_s=1.0, seed=21)
+    W, blocked = _weights_both(cfg, dev)
+    logits, x = synth.make_routing_inputs(cfg)
+    got = _run(cfg, dev, blocked, True)
+    ref = oracle.layer(logits, x, cfg.act, W.raw, cfg.w, cfg.k)
+    assert np.array_equal(got["topk_ids"].numpy(), ref["topk_ids"])
+    assert np.array_equal(got["offsets"].numpy(), ref["offsets"])
+    err = oracle.rel_max_err(got["y"].numpy(), ref["y"])
+    assert err <= H.TOL["fp8_e4m3fn"], err

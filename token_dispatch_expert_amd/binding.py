@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libmoe.so"
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_BF16_BLOCKED = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_BF16_BLOCKED, MOE_FP8_E4M3FN_BLOCKED = 0, 1, 2, 3, 4
 
 _DTYPE_ENUM = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16,
                torch.float8_e4m3fn: MOE_FP8_E4M3FN, torch.uint8: MOE_FP8_E4M3FN}
@@ -70,7 +70,7 @@ def load_library(path: str | None = None):
         "moe_route_gemm_workspace_size": ([I, I, I], S),
         "moe_permute_capped": ([P, I, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "moe_permute_noalloc": ([P, I, P, I, I, I, I, P, P, P, P, P, P], I),
-        "moe_block_weights": ([P, P, I, I, I, P], I),
+        "moe_block_weights": ([P, P, I, I, I, I, P], I),
         "moe_layer_capped": ([P, P, I, I, I, I, I, I, I, P, P, P, I, P, P, P,
                               P, P, P, P, P, P, P, P, P, I, P, S, P], I),
     }
@@ -238,16 +238,16 @@ def moe_expert_capacity(T: int, E: int, k: int, factor_percent: int) -> int:
 
 
 def _weights(w_gate, w_up, w_down, s_gate, s_up, s_down, blocked=False):
-    """blocked: the bf16 weights are in the MOE_BF16_BLOCKED layout (see moe_block_weights); the
+    """blocked: the bf16 or fp8 weights are in their blocked layout (see moe_block_weights); the
     tensors keep their [E, d_ff, d] / [E, d, d_ff] shapes."""
     E, d_ff, d = w_gate.shape
     _need(w_up, w_gate.dtype, (E, d_ff, d), "w_up")
     _need(w_down, w_gate.dtype, (E, d, d_ff), "w_down")
     w_dt = _dt(w_gate, "w_gate")
     if blocked:
-        if w_dt != MOE_BF16:
-            raise TypeError("blocked weights are bfloat16")
-        w_dt = MOE_BF16_BLOCKED
+        if w_dt not in (MOE_BF16, MOE_FP8_E4M3FN):
+            raise TypeError("blocked weights are bfloat16 or float8_e4m3fn")
+        w_dt = MOE_BF16_BLOCKED if w_dt == MOE_BF16 else MOE_FP8_E4M3FN_BLOCKED
     if w_dt == MOE_FP8_E4M3FN:
         for s, shp, n in ((s_gate, (E, -(-d_ff // 128), -(-d // 128)), "s_gate"),
                           (s_up, (E, -(-d_ff // 128), -(-d // 128)), "s_up"),
@@ -259,13 +259,16 @@ def _weights(w_gate, w_up, w_down, s_gate, s_up, s_down, blocked=False):
 
 
 def moe_block_weights(src, dst, stream=None):
-    """dst [E, N, K] bf16 <- src [E, N, K] bf16 in the MOE_BF16_BLOCKED layout."""
+    """dst [E, N, K] <- src [E, N, K] (bfloat16 or float8_e4m3fn) in its blocked layout."""
     if src.dim() != 3:
         raise ValueError("src: expected [E, N, K]")
     E, N, K = src.shape
-    _need(src, torch.bfloat16, (E, N, K), "src")
-    _need(dst, torch.bfloat16, (E, N, K), "dst")
-    _check(load_library().moe_block_weights(_ptr(src), _ptr(dst), E, N, K, _stream(stream)))
+    if src.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError(f"src: expected bfloat16 or float8_e4m3fn, got {src.dtype}")
+    _need(src, src.dtype, (E, N, K), "src")
+    _need(dst, src.dtype, (E, N, K), "dst")
+    _check(load_library().moe_block_weights(_ptr(src), _ptr(dst), _dt(src, "src"), E, N, K,
+                                            _stream(stream)))
 
 
 def moe_grouped_ffn(x_sorted, offsets, w_gate, w_up, w_down, y_sorted, workspace: Workspace,

@@ -136,18 +136,23 @@ moe_status_t check_ffn(const void* x_sorted, moe_dtype_t act, const int32_t* off
   if (act == MOE_F32) {
     if (wdt != MOE_F32) return MOE_ERR_UNSUPPORTED;
   } else if (act == MOE_BF16) {
-    if (wdt != MOE_BF16 && wdt != MOE_FP8_E4M3FN && wdt != MOE_BF16_BLOCKED) return MOE_ERR_UNSUPPORTED;
+    if (wdt != MOE_BF16 && wdt != MOE_FP8_E4M3FN && wdt != MOE_BF16_BLOCKED &&
+        wdt != MOE_FP8_E4M3FN_BLOCKED)
+      return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
-  const int mult = wdt == MOE_FP8_E4M3FN ? 128 : (wdt == MOE_BF16_BLOCKED ? 64 : 8);
+  const bool fp8 = wdt == MOE_FP8_E4M3FN || wdt == MOE_FP8_E4M3FN_BLOCKED;
+  const int mult = fp8 ? 128 : (wdt == MOE_BF16_BLOCKED ? 64 : 8);
+  // blocked fp8 runs on the direct-to-LDS tiles only, which stage scales for contractions up to this
+  if (wdt == MOE_FP8_E4M3FN_BLOCKED && (d > 65536 || d_ff > 65536)) return MOE_ERR_UNSUPPORTED;
   if (d % mult != 0 || d_ff % mult != 0) return MOE_ERR_UNSUPPORTED;
   const long long wel = (long long)E * d * d_ff;
   if (!ok_ptr(x_sorted, (long long)rows * d, 16) || !ok_ptr(offsets, E + 1, 4) ||
       !ok_ptr(wg, wel, 16) || !ok_ptr(wu, wel, 16) || !ok_ptr(wd, wel, 16) ||
       !ok_ptr(y_sorted, (long long)rows * d, 16))
     return MOE_ERR_INVALID_ARG;
-  if (wdt == MOE_FP8_E4M3FN) {
+  if (fp8) {
     const long long ns = (long long)E * (d / 128) * (d_ff / 128);
     if (!ok_ptr(sg, ns, 4) || !ok_ptr(su, ns, 4) || !ok_ptr(sd, ns, 4)) return MOE_ERR_INVALID_ARG;
   } else if (sg || su || sd) {
@@ -304,16 +309,21 @@ moe_status_t moe_grouped_ffn(const void* x_sorted, moe_dtype_t act_dtype, const 
   return hip_status(moe::launch_grouped_ffn(a, dev, static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_block_weights(const void* src, void* dst, int E, int N, int K, void* stream) {
-  if (E < 1 || N < 8 || K < 64 || N % 8 != 0 || K % 64 != 0) return MOE_ERR_INVALID_ARG;
-  if ((long long)N * K >= (1LL << 30)) return MOE_ERR_INVALID_ARG;  // one matrix under 2 GiB
+moe_status_t moe_block_weights(const void* src, void* dst, moe_dtype_t w_dtype, int E, int N, int K,
+                               void* stream) {
+  if (w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+  const int esize = w_dtype == MOE_BF16 ? 2 : 1;
+  const int B = 128 / esize;  // contraction elements per block row (128 bytes)
+  if (E < 1 || N < 8 || K < B || N % 8 != 0 || K % B != 0) return MOE_ERR_INVALID_ARG;
+  if ((long long)N * K * esize >= (1LL << 31)) return MOE_ERR_INVALID_ARG;  // one matrix under 2 GiB
   const long long n = (long long)E * N * K;
   if (n >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
   if (!ok_ptr(src, n, 16) || !ok_ptr(dst, n, 16)) return MOE_ERR_INVALID_ARG;
   const char* s0 = static_cast<const char*>(src);
   const char* d0 = static_cast<const char*>(dst);
-  if (s0 < d0 + 2 * n && d0 < s0 + 2 * n) return MOE_ERR_INVALID_ARG;  // overlap
-  return hip_status(moe::launch_block_weights(src, dst, E, N, K, static_cast<hipStream_t>(stream)));
+  if (s0 < d0 + esize * n && d0 < s0 + esize * n) return MOE_ERR_INVALID_ARG;  // overlap
+  return hip_status(moe::launch_block_weights(src, dst, E, N, (long long)K * esize,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_combine(const float* y_sorted, const int32_t* flat_to_sorted,

@@ -495,8 +495,8 @@ struct TiledArgs {
   // prefill: 1 when ffn_lean_kernel runs beside this launch on a second stream and may take the
   // experts with at most kStreamMaxRows rows (both kernels decide from the counts alike)
   int lean = 0;
-  // bf16 weights in the MOE_BF16_BLOCKED layout ([N/8][K/64][8][64]); only read by the bf16
-  // direct-to-LDS tiles with 64-wide steps and the lean kernel
+  // weights in a blocked layout (8 rows x 128 bytes per 1 KB block); only read by the
+  // direct-to-LDS tiles whose steps take 128 bytes of a weight row, and the lean kernel
   int wblk = 0;
 };
 
@@ -879,7 +879,8 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
                 "decode contraction split: bf16 weights, tiles of at most 64 x 128");
   constexpr bool F8 = WF == kFP8;
   constexpr int WB = F8 ? 1 : 2;                        // weight bytes per element
-  constexpr bool BLKOK = WF == kBF16 && DK == 64;        // shapes that read blocked weights
+  constexpr bool BLKOK = DK * WB == 128;                 // a step reads 128 bytes of a B row:
+                                                        // the shapes that read blocked weights
   constexpr int NW = WGM * WGN, NTH = 64 * NW;
   constexpr int TM = WGM * WM, TN = WGN * WN;
   constexpr int MF = WM / 16, NF = WN / 16;
@@ -1099,7 +1100,7 @@ __device__ __forceinline__ void dl_tiles(const TiledArgs& p, unsigned char* smem
         // blocked weights: a load instruction's 8 rows (b_row(t) & 7 is this lane's row among
         // them, the first is a multiple of 8) are one 1 KB block per step, row r at r * 128
         if constexpr (BLKOK)
-          if (p.wblk) b_lane = (b_row(t) & ~7) * p.K * 2 + (b_row(t) & 7) * 128 + c * 16;
+          if (p.wblk) b_lane = (b_row(t) & ~7) * p.K * WB + (b_row(t) & 7) * 128 + c * 16;
       }
       const int t0w = wave * RPB;  // first B row of this wave's instruction 0 (wave-uniform)
       // bytes between steps in a B row: DK elements, or one 1 KB block (blocked weights)
@@ -1679,7 +1680,9 @@ static size_t tail_partial_bytes(moe_dtype_t wdt) {
 }
 
 size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt) {
-  if (wdt == MOE_BF16_BLOCKED) wdt = MOE_BF16;  // the same kernels and workspace
+  // the blocked layouts: the same kernels and workspace as their row-major formats
+  if (wdt == MOE_BF16_BLOCKED) wdt = MOE_BF16;
+  if (wdt == MOE_FP8_E4M3FN_BLOCKED) wdt = MOE_FP8_E4M3FN;
   const size_t hb = act == MOE_F32 ? 4 : 2;
   const size_t h = align_up((size_t)rows * d_ff * hb, 256);
   if (uses_split(rows, E, d, d_ff, act, wdt)) return h + kPartialBytes;
@@ -1712,11 +1715,14 @@ static hipError_t launch_split(TiledArgs p, const DeviceInfo& dev, hipStream_t s
 
 hipError_t launch_grouped_ffn(const FfnArgs& a_in, const DeviceInfo& dev, hipStream_t stream) {
   if (a_in.rows == 0) return hipSuccess;
-  // blocked bf16 weights run the bf16 kernels with the blocked addressing (validated: d and d_ff
-  // multiples of 64, so every bf16 tiled path below reads them, none of the streaming kernel's)
+  // blocked weights run their format's kernels with the blocked addressing. Validated: bf16 d
+  // and d_ff multiples of 64, so every bf16 tiled path below reads them, none of the streaming
+  // kernel's; fp8 d and d_ff at most 65536, so the direct-to-LDS tiles take every fp8 expert
+  // (also in the smallest launches, which otherwise stream their <= 16-row experts)
   FfnArgs a = a_in;
-  const int wblk = a.wdt == MOE_BF16_BLOCKED ? 1 : 0;
-  if (wblk) a.wdt = MOE_BF16;
+  const int wblk = (a.wdt == MOE_BF16_BLOCKED || a.wdt == MOE_FP8_E4M3FN_BLOCKED) ? 1 : 0;
+  if (a.wdt == MOE_BF16_BLOCKED) a.wdt = MOE_BF16;
+  if (a.wdt == MOE_FP8_E4M3FN_BLOCKED) a.wdt = MOE_FP8_E4M3FN;
   // Which kernel takes which expert (decided per expert on the device from its row count):
   //  - fp32, or widths that are not multiples of 64: the streaming kernel takes every expert;
   //  - decode-sized batches (T*k < 32*E with bf16 weights, T*k <= 8*E with fp8 weights): the
@@ -1730,7 +1736,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, const DeviceInfo& dev, hipStr
   // that bf16 would split the contraction (at most a few rows in all), where streaming the
   // small experts, whose kernel splits each item's contraction over its waves, is faster
   const bool fp8_dl_small = a.wdt == MOE_FP8_E4M3FN && tiled && !big && a.d <= kFp8DlMaxK &&
-                            a.d_ff <= kFp8DlMaxK && !split_gemm(a.rows, a.E, a.d_ff, 64);
+                            a.d_ff <= kFp8DlMaxK && (wblk || !split_gemm(a.rows, a.E, a.d_ff, 64));
   if (tiled && !big && (a.wdt == MOE_BF16 || fp8_dl_small)) small = 0;
   StreamArgs gu{a.x_sorted, a.w_gate, a.w_up, a.s_gate, a.s_up, a.h, a.offsets,
                 a.E, a.d, a.d_ff, a.rows, small};
@@ -1835,26 +1841,28 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, const DeviceInfo& dev, hipStr
   return st;
 }
 
-// MOE_BF16_BLOCKED weights from row-major ones: one thread per 16-byte piece (8 elements) of the
-// destination, in destination order, so the stores are contiguous and each source row piece is
-// read by one thread.
+// Blocked weights from row-major ones (8 rows x 128 bytes per block): one thread per 16-byte
+// piece of the destination, in destination order, so the stores are contiguous and each source
+// piece is read by one thread.
 __global__ __launch_bounds__(256) void block_weights_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                            int N, int K, long long pieces) {
+                                                            long long row_bytes, long long pieces) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= pieces) return;
-  // destination piece i: (e, n/8, k/64) block, row n%8 of it, 8-element piece c of that row
+  // destination piece i: block (e, n/8, 128-byte column c8), row n%8 of it, 16-byte piece c
   const int c = (int)(i & 7), r = (int)((i >> 3) & 7);
-  const long long blk = i >> 6;                  // (e * (N/8) + n/8) * (K/64) + k/64
-  const int kb = (int)(blk % (K / 64));
-  const long long row = blk / (K / 64) * 8 + r;  // e * N + n
-  dst[i] = src[(row * K + (long long)kb * 64 + c * 8) / 8];
+  const long long blk = i >> 6;                    // (e * (N/8) + n/8) * (row_bytes/128) + c8
+  const long long per_row = row_bytes / 128;
+  const long long c8 = blk % per_row;
+  const long long row = blk / per_row * 8 + r;     // e * N + n
+  dst[i] = src[(row * row_bytes + c8 * 128 + c * 16) / 16];
 }
 
-hipError_t launch_block_weights(const void* src, void* dst, int E, int N, int K, hipStream_t stream) {
-  const long long pieces = (long long)E * N * K / 8;
+hipError_t launch_block_weights(const void* src, void* dst, int E, int N, long long row_bytes,
+                                hipStream_t stream) {
+  const long long pieces = (long long)E * N * row_bytes / 16;
   const unsigned grid = (unsigned)((pieces + 255) / 256);
   block_weights_kernel<<<grid, 256, 0, stream>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
-                                                 N, K, pieces);
+                                                 row_bytes, pieces);
   return hipGetLastError();
 }
 

@@ -95,8 +95,10 @@ struct FfnArgs {
   void* h;  // [rows, d_ff] in act dtype (workspace)
 };
 size_t ffn_workspace_bytes(int rows, int E, int d, int d_ff, moe_dtype_t act, moe_dtype_t wdt);
-// bf16 [E, N, K] row-major -> [E][N/8][K/64][8][64] (N % 8 == 0, K % 64 == 0, E*N*K < 2^31)
-hipError_t launch_block_weights(const void* src, void* dst, int E, int N, int K, hipStream_t stream);
+// [E, N, row_bytes] row-major -> [E][N/8][row_bytes/128][8][128 bytes] (N % 8 == 0,
+// row_bytes % 128 == 0): the blocked weight layouts
+hipError_t launch_block_weights(const void* src, void* dst, int E, int N, long long row_bytes,
+                                hipStream_t stream);
 hipError_t launch_grouped_ffn(const FfnArgs& a, const DeviceInfo& dev, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* flat_to_sorted,

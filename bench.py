@@ -168,6 +168,14 @@ def expert_time_sweep(args) -> int:
                    "s_up": torch.full((E, d_ff // 128, d // 128), 1.0 / (64 * d ** 0.5), device=dev),
                    "s_down": torch.full((E, d // 128, d_ff // 128), 1.0 / (64 * d_ff ** 0.5), device=dev)}
             ridge = 2500e12 / 8e12 / 2
+        # the weights in their blocked layout, as the layer benchmark uses them (row-major with
+        # --row-major-weights)
+        if not args.row_major_weights:
+            for i in range(3):
+                b = torch.empty_like(W[i])
+                moe.moe_block_weights(W[i], b)
+                W[i] = b
+            skw["weights_blocked"] = True
         pts = []
         for G in Gs:
             for n in ns:
@@ -191,6 +199,7 @@ def expert_time_sweep(args) -> int:
         wbytes = 3 * d * d_ff * (2 if wfmt == "bf16" else 1)
         result["shapes"].append({
             "shape": name, "d": d, "d_ff": d_ff, "E": E, "weights": wfmt,
+            "weight_layout": "row-major" if args.row_major_weights else "blocked (8 rows x 128 bytes)",
             "points": [{"G": int(G), "n": int(n), "us": round(us, 2)} for G, n, _, us in pts],
             "fit": {"a_us": round(a, 2), "b_us_per_expert": round(b, 3), "c_us": round(c, 2),
                     "beta_us_per_row": round(beta, 5), "max_rel_misfit": round(mx, 3),

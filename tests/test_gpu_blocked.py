@@ -5,9 +5,9 @@ and whole layers with blocked weights against the same layers with row-major wei
 same kernels run, the arithmetic is the same, so every output must be bit-identical, on every
 kernel path that reads bf16 weights (decode-sized tiles, their contraction split, the prefill
 kernel's large tiles and streaming role, and the lean kernel on the second stream) and fp8
-weights (decode-sized and prefill tiles). The smallest fp8 launches, whose row-major weights
-stream their few-row experts on another kernel (another summation order), are checked against
-the fp64 oracle."""
+weights (decode-sized and prefill tiles), and the full-size prefill layers as the benchmark
+times them. The smallest fp8 launches, whose row-major weights stream their few-row experts on
+another kernel (another summation order), are checked against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -135,3 +135,46 @@ def test_blocked_fp8_smallest_launch_against_oracle(dev):
     assert np.array_equal(got["offsets"].numpy(), ref["offsets"])
     err = oracle.rel_max_err(got["y"].numpy(), ref["y"])
     assert err <= H.TOL["fp8_e4m3fn"], err
+
+
+def _device_weights(cfg, dev, seed=0):
+    """Seeded weights drawn on the device for all E experts (no host copies: this comparison
+    needs no oracle), in the row-major layout, and their blocked copies."""
+    g = torch.Generator(device=dev).manual_seed(seed)
+    fp8 = cfg.w == "fp8_e4m3fn"
+
+    def mat(N, K):
+        out = torch.empty((cfg.E, N, K), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16, device=dev)
+        for e0 in range(0, cfg.E, 32):
+            w = torch.randn((min(32, cfg.E - e0), N, K), generator=g, device=dev)
+            out[e0:e0 + 32] = w.mul_(64.0).clamp_(-448, 448).to(out.dtype) if fp8 else w.div_(K ** 0.5).to(out.dtype)
+        return out
+
+    W = [mat(cfg.d_ff, cfg.d), mat(cfg.d_ff, cfg.d), mat(cfg.d, cfg.d_ff)]
+    skw = {}
+    if fp8:
+        for n, (N, K) in zip(("s_gate", "s_up", "s_down"), ((cfg.d_ff, cfg.d), (cfg.d_ff, cfg.d), (cfg.d, cfg.d_ff))):
+            skw[n] = torch.rand((cfg.E, N // 128, K // 128), generator=g, device=dev).add_(0.5).div_(64 * K ** 0.5)
+    blocked = []
+    for w in W:
+        b = torch.empty_like(w)
+        moe.moe_block_weights(w, b)
+        blocked.append(b)
+    torch.cuda.synchronize()
+    return (*W, skw), (*blocked, skw)
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_blocked_full_size_matches_row_major(dev, name):
+    # the full-size prefill layers in the configuration the benchmark times (blocked weights):
+    # every output bit-identical to the same layer with row-major weights, whose parity against
+    # the oracle the full-size sampled tests check
+    cfg = synth.CONFIGS[name]
+    row_major, blocked = _device_weights(cfg, dev)
+    ref = _run(cfg, dev, row_major, False)
+    got = _run(cfg, dev, blocked, True)
+    assert bool(torch.isfinite(ref["y"]).all())
+    for n in ref:
+        assert torch.equal(got[n].view(torch.uint8), ref[n].view(torch.uint8)), n
+    del row_major, blocked
+    torch.cuda.empty_cache()

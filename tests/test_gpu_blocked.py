@@ -5,7 +5,7 @@ and whole layers with blocked weights against the same layers with row-major wei
 same kernels run, the arithmetic is the same, so every output must be bit-identical, on every
 kernel path that reads bf16 weights (decode-sized tiles, their contraction split, the prefill
 kernel's large tiles and streaming role, and the lean kernel on the second stream) and fp8
-weights (decode-sized and prefill tiles), and the full-size prefill layers as the benchmark
+weights (decode-sized and prefill tiles), and the full-size c3-c5 layers as the benchmark
 times them. The smallest fp8 launches, whose row-major weights stream their few-row experts on
 another kernel (another summation order), are checked against the fp64 oracle."""
 import numpy as np
@@ -164,9 +164,9 @@ def _device_weights(cfg, dev, seed=0):
     return (*W, skw), (*blocked, skw)
 
 
-@pytest.mark.parametrize("name", ["c4", "c5"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
 def test_blocked_full_size_matches_row_major(dev, name):
-    # the full-size prefill layers in the configuration the benchmark times (blocked weights):
+    # the full-size decode (c3) and prefill layers in the configuration the benchmark times (blocked weights):
     # every output bit-identical to the same layer with row-major weights, whose parity against
     # the oracle the full-size sampled tests check
     cfg = synth.CONFIGS[name]

@@ -19,7 +19,9 @@
  *    stream has reached that point. Prefill-sized calls of moe_grouped_ffn with bf16 weights
  *    (and the moe_layer calls that make them) may run the experts with few rows on a second
  *    stream, one that the library creates for each (device, caller stream) on first use and
- *    keeps until the process ends: it waits on an event recorded on `stream` at the start of
+ *    keeps until the process ends (for at most 64 such pairs per process; calls on further
+ *    caller streams run on `stream` alone, with results equal up to rounding): it
+ *    waits on an event recorded on `stream` at the start of
  *    the call, and `stream` waits on an event recorded on it at the end, so everything
  *    enqueued on `stream` afterwards sees the call's results, and the call can be captured in
  *    a graph. Calls on one caller stream must not be enqueued from several threads at once

@@ -60,24 +60,27 @@ def _poison(out):
 ], ids=["c2", "decode-split", "prefill", "prefill-second-stream", "fp8-decode", "fp8-prefill"])
 def test_layer_graph_replay_matches_eager(dev, cfg):
     fn, out = _layer_fn(cfg, dev)
-    fn()
-    torch.cuda.synchronize()
+    # every eager call runs on the stream the graph is captured on: the library keys its second
+    # stream by the caller's stream, so eager calls and the capture take the same schedule
+    s = torch.cuda.Stream()
+
+    def eager():
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+    eager()
     ref = {k: v.clone() for k, v in out.items()}
     # a second eager call gives the same bits (the reference is stable)
     _poison(out)
-    fn()
-    torch.cuda.synchronize()
+    eager()
     for k in out:
         assert torch.equal(out[k].view(torch.uint8), ref[k].view(torch.uint8)), k
 
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         fn()
     torch.cuda.synchronize()
 

@@ -31,6 +31,8 @@ hipError_t device_info(DeviceInfo* out) {
   return hipSuccess;
 }
 
+constexpr size_t kMaxSideStreams = 64;  // (device, caller stream) pairs with a second stream
+
 bool side_stream_for(hipStream_t caller, SideStream* out) {
   static std::mutex mu;
   struct Entry { int dev; hipStream_t caller; SideStream side; };
@@ -43,6 +45,9 @@ bool side_stream_for(hipStream_t caller, SideStream* out) {
       *out = en.side;
       return true;
     }
+  // The table is never pruned (a caller stream may be destroyed and its handle reused), so it
+  // is bounded: past kMaxSideStreams pairs a call takes the one-stream schedule instead.
+  if (table.size() >= kMaxSideStreams) return false;
   // Creating a stream and events is allowed while a graph is being captured once this thread's
   // capture mode is relaxed (the documented way to make such calls during a capture); the
   // previous mode is restored afterwards.

@@ -75,6 +75,42 @@ def test_block_weights_beyond_2g_elements(dev):
     del src, dst
 
 
+def test_block_weights_beyond_2p32_pieces(dev):
+    # a tensor of more 16-byte pieces than one dispatch has threads (2^32): 2,400 experts of
+    # 2048 x 7168 bf16, 70.5 GB each for source and destination
+    E, N, K = 2400, 2048, 7168
+    assert E * N * K * 2 // 16 > 2 ** 32
+    need = 2 * E * N * K * 2
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(dev)
+    if free < need + (8 << 30):
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
+    src = torch.empty((E, N, K), dtype=torch.int16, device=dev)
+    g = torch.Generator(device=dev).manual_seed(8)
+    for e0 in range(0, E, 200):
+        src[e0:e0 + 200].random_(-32768, 32767, generator=g)
+    dst = torch.empty_like(src)
+    moe.moe_block_weights(src.view(torch.bfloat16), dst.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    e = torch.from_numpy(rng.integers(0, E, 8192)).to(dev)
+    n = torch.from_numpy(rng.integers(0, N, 8192)).to(dev)
+    k = torch.from_numpy(rng.integers(0, K, 8192)).to(dev)
+    # every element of the last block, and of the first block past 2^32 pieces (2^36 bytes)
+    first = (2 ** 36) // 2 // 512 * 512                 # an element index at a block start
+    blk = first // 512
+    kb = blk % (K // 64); nb = blk // (K // 64) % (N // 8); eb = blk // (K // 64) // (N // 8)
+    idx = torch.arange(512, device=dev)
+    e = torch.cat([e, torch.full((512,), E - 1, device=dev), torch.full((512,), eb, device=dev)])
+    n = torch.cat([n, N - 8 + idx // 64, nb * 8 + idx // 64])
+    k = torch.cat([k, K - 64 + idx % 64, kb * 64 + idx % 64])
+    pos = ((e * (N // 8) + n // 8) * (K // 64) + k // 64) * 512 + (n % 8) * 64 + k % 64
+    assert int(pos.max()) == E * N * K - 1
+    assert torch.equal(dst.view(-1)[pos], src[e, n, k])
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def _run(cfg, dev, W, blocked):
     logits, x = synth.make_routing_inputs(cfg)
     lg = torch.from_numpy(logits).to(dev)

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["route.hip", "router.hip", "permute.hip", "ffn.hip", "combine.hip", "api.cpp"]
+SOURCES = ["route.hip", "router.hip", "permute.hip", "ffn.hip", "combine.hip", "layout.hip", "api.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code; the host pass ignores the feature.
 FLAGS = [

@@ -1841,29 +1841,4 @@ hipError_t launch_grouped_ffn(const FfnArgs& a_in, const DeviceInfo& dev, hipStr
   return st;
 }
 
-// Blocked weights from row-major ones (8 rows x 128 bytes per block): one thread per 16-byte
-// piece of the destination, in destination order, so the stores are contiguous and each source
-// piece is read by one thread.
-__global__ __launch_bounds__(256) void block_weights_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                            long long row_bytes, long long pieces) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= pieces) return;
-  // destination piece i: block (e, n/8, 128-byte column c8), row n%8 of it, 16-byte piece c
-  const int c = (int)(i & 7), r = (int)((i >> 3) & 7);
-  const long long blk = i >> 6;                    // (e * (N/8) + n/8) * (row_bytes/128) + c8
-  const long long per_row = row_bytes / 128;
-  const long long c8 = blk % per_row;
-  const long long row = blk / per_row * 8 + r;     // e * N + n
-  dst[i] = src[(row * row_bytes + c8 * 128 + c * 16) / 16];
-}
-
-hipError_t launch_block_weights(const void* src, void* dst, int E, int N, long long row_bytes,
-                                hipStream_t stream) {
-  const long long pieces = (long long)E * N * row_bytes / 16;
-  const unsigned grid = (unsigned)((pieces + 255) / 256);
-  block_weights_kernel<<<grid, 256, 0, stream>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
-                                                 row_bytes, pieces);
-  return hipGetLastError();
-}
-
 }  // namespace moe
